@@ -1,0 +1,5 @@
+"""CPU oracle (test infrastructure only): see oracle.lora_oracle."""
+from .lora_oracle import (  # noqa: F401
+    decode, build_addressing, shrink, gather_shrink, expand, apply, apply_linear,
+    shrink_all_slots, apply_scalar, run_target, within_tolerance,
+)
