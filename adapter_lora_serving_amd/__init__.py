@@ -1,0 +1,276 @@
+"""Batched multi-LoRA delta on MI355X: Python binding of liblora_mi355x.so.
+
+The functions here only marshal arguments (torch tensors -> device pointers,
+torch's current HIP stream) and call the C ABI declared in
+include/lora_mi355x.h; every step of the computation runs in the HIP kernels
+of the library. There is no fallback: if the library is not built, or no GPU
+is present, the calls raise.
+
+Names and argument order follow the LoraBackend methods of the mstar
+lora.backend page (shrink, gather_shrink, expand_fused, apply_linear_,
+apply_), plus build_addressing for the per-step addressing that page says both
+kernels read.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from collections import namedtuple
+from typing import Optional, Sequence
+
+__all__ = [
+    "Addressing", "LoraError", "lib", "lib_path", "build_addressing", "shrink",
+    "gather_shrink", "expand_", "expand_fused", "apply_linear_", "apply_", "Backend",
+    "workspace_bytes", "STATUS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
+_LIB = None
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "alignment", 4: "workspace",
+          5: "HIP launch failed"}
+
+Addressing = namedtuple("Addressing", ["token_order", "slot_indptr"])
+
+# symbol -> (restype, argtypes); mirrors include/lora_mi355x.h
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lora_version": (ctypes.c_char_p, []),
+    "lora_build_addressing": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "lora_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P,
+                                   _P, _P, _P]),
+    "lora_gather_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _P, _P,
+                                          _P, _P, _P]),
+    "lora_expand": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P,
+                                   _P, _P, _P]),
+    "lora_apply_linear": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P, _P,
+                                         _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lora_apply_linear_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+}
+
+
+class LoraError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load the HIP library (after torch, so both use the same HIP runtime)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise LoraError(f"{_LIB_PATH} is not built: run `python -m adapter_lora_serving_amd.build`"
+                            " (the LoRA delta has no CPU or PyTorch fallback)")
+        import torch  # noqa: F401  (loads torch's libamdhip64 first)
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().lora_status_string(status).decode()
+        raise LoraError(f"{what}: {msg} (status {status})")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype == torch.float32:
+        return 0
+    raise LoraError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(*tensors):
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise LoraError("all tensors must be on the GPU (no CPU fallback)")
+        if not t.is_contiguous():
+            raise LoraError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise LoraError("tensors on different devices")
+    return dev
+
+
+def _stream(dev) -> int:
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _i32(t):
+    import torch
+    return t if t.dtype == torch.int32 else t.to(torch.int32)
+
+
+def _addr(addressing):
+    if isinstance(addressing, Addressing):
+        return addressing.token_order, addressing.slot_indptr
+    return addressing[0], addressing[1]
+
+
+def build_addressing(token_slot, slots: int, out: Optional[Addressing] = None) -> Addressing:
+    """Group a step's tokens by adapter slot on the device (no host sync)."""
+    import torch
+    token_slot = _i32(token_slot)
+    dev = _dev(token_slot)
+    T = token_slot.numel()
+    if out is None:
+        out = Addressing(torch.empty(T, dtype=torch.int32, device=dev),
+                         torch.empty(slots + 1, dtype=torch.int32, device=dev))
+    _dev(token_slot, *out)
+    st = lib().lora_build_addressing(_ptr(token_slot), T, slots, _ptr(out.token_order),
+                                     _ptr(out.slot_indptr), _stream(dev))
+    _check(st, "lora_build_addressing")
+    return out
+
+
+def shrink(x, a, addressing, ranks, num_slices: int = 1, out=None):
+    """h[t] = x[t] @ a[slot(t)]^T (float32 [T, num_slices*R])."""
+    import torch
+    order, indptr = _addr(addressing)
+    ranks = _i32(ranks)
+    dev = _dev(x, a, order, indptr, ranks)
+    T, in_f = x.shape
+    slots, SR, in_a = a.shape
+    if in_a != in_f or SR % num_slices or a.dtype != x.dtype:
+        raise LoraError("shape/dtype mismatch between x and a")
+    R = SR // num_slices
+    if out is None:
+        out = torch.empty(T, SR, dtype=torch.float32, device=dev)
+    st = lib().lora_shrink(_dtype_code(x), _ptr(x), T, in_f, _ptr(a), slots, num_slices, R,
+                           _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(out), _stream(dev))
+    _check(st, "lora_shrink")
+    return out
+
+
+def gather_shrink(ids, a, addressing, ranks, out=None):
+    """h[t] = a[slot(t)][:, ids[t]] (float32 [T, R]); invalid ids give 0."""
+    import torch
+    order, indptr = _addr(addressing)
+    ids = _i32(ids)
+    ranks = _i32(ranks)
+    dev = _dev(ids, a, order, indptr, ranks)
+    T = ids.numel()
+    slots, R, vocab = a.shape
+    if out is None:
+        out = torch.empty(T, R, dtype=torch.float32, device=dev)
+    st = lib().lora_gather_shrink(_dtype_code(a), _ptr(ids), T, vocab, _ptr(a), slots, R,
+                                  _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(out), _stream(dev))
+    _check(st, "lora_gather_shrink")
+    return out
+
+
+def _slices(out_slices: Sequence[int]):
+    arr = (ctypes.c_int64 * len(out_slices))(*[int(w) for w in out_slices])
+    return arr, len(out_slices)
+
+
+def expand_(h, b, addressing, ranks, scalings, y, out_slices: Sequence[int]) -> None:
+    """y[t, slice i] += scalings[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T."""
+    order, indptr = _addr(addressing)
+    ranks = _i32(ranks)
+    dev = _dev(h, b, order, indptr, ranks, scalings, y)
+    T = y.shape[0]
+    slots, out, R = b.shape
+    if sum(out_slices) != out or y.shape[1] != out or b.dtype != y.dtype:
+        raise LoraError("shape/dtype mismatch between y, b and out_slices")
+    arr, S = _slices(out_slices)
+    st = lib().lora_expand(_dtype_code(y), _ptr(y), T, ctypes.cast(arr, _P), S, _ptr(h), _ptr(b),
+                           slots, R, _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(scalings),
+                           _stream(dev))
+    _check(st, "lora_expand")
+
+
+expand_fused = expand_
+
+_WS = {}
+
+
+def workspace_bytes(T: int, in_features: int, slots: int, num_slices: int, R: int) -> int:
+    return int(lib().lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R))
+
+
+def _workspace(dev, nbytes: int):
+    """A zero-filled workspace cached per device; the library leaves its
+    counters at zero after every completed call, so it is reused as is."""
+    import torch
+    key = (str(dev), torch.cuda.current_stream(dev).cuda_stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS[key] = ws
+    return ws
+
+
+def apply_linear_(x, y, a, b, addressing, ranks, scalings, out_slices: Sequence[int],
+                  workspace=None) -> None:
+    """Shrink then expand into y for a linear target (fused where the library fuses)."""
+    order, indptr = _addr(addressing)
+    ranks = _i32(ranks)
+    dev = _dev(x, y, a, b, order, indptr, ranks, scalings)
+    T, in_f = x.shape
+    slots, out, R = b.shape
+    S = len(out_slices)
+    if a.shape != (slots, S * R, in_f) or y.shape != (T, out) or sum(out_slices) != out:
+        raise LoraError("shape mismatch in apply_linear_")
+    need = workspace_bytes(T, in_f, slots, S, R)
+    ws = _workspace(dev, need) if workspace is None else workspace
+    arr, S = _slices(out_slices)
+    st = lib().lora_apply_linear(_dtype_code(x), _ptr(x), _ptr(y), T, in_f, ctypes.cast(arr, _P), S,
+                                 _ptr(a), _ptr(b), slots, R, _ptr(order), _ptr(indptr), _ptr(ranks),
+                                 _ptr(scalings), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(dev))
+    _check(st, "lora_apply_linear")
+
+
+def apply_(x, y, a, b, addressing, ranks, scalings, out_slices: Sequence[int],
+           embedding: bool = False):
+    """Shrink (a gather for an embedding target, whose x is token ids) then
+    expand into y; returns y."""
+    if embedding:
+        h = gather_shrink(x, a, addressing, ranks)
+        expand_(h, b, addressing, ranks, scalings, y, out_slices)
+    else:
+        apply_linear_(x, y, a, b, addressing, ranks, scalings, out_slices)
+    return y
+
+
+class Backend:
+    """The LoraBackend method surface of the lora.backend page, on MI355X."""
+
+    def shrink(self, x, a, addressing, ranks, num_slices: int = 1):
+        return shrink(x, a, addressing, ranks, num_slices)
+
+    def gather_shrink(self, ids, a, addressing, ranks):
+        return gather_shrink(ids, a, addressing, ranks)
+
+    def expand_fused(self, h, b, addressing, ranks, scalings, y, out_slices):
+        expand_(h, b, addressing, ranks, scalings, y, out_slices)
+
+    def apply_linear_(self, x, y, a, b, addressing, ranks, scalings, out_slices):
+        apply_linear_(x, y, a, b, addressing, ranks, scalings, out_slices)
+
+    def apply_(self, x, y, a, b, addressing, ranks, scalings, out_slices, embedding=False):
+        return apply_(x, y, a, b, addressing, ranks, scalings, out_slices, embedding)

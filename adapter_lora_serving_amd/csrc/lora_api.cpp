@@ -1,0 +1,179 @@
+// C ABI of the batched multi-LoRA delta: argument validation on the host
+// (scalars, pointers and alignment only; device data is never read here) and
+// kernel launches on the caller's stream. Nothing is allocated and nothing
+// synchronises, so every entry point can be recorded in a hipGraph.
+#include "lora_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include "lora_kernels.h"
+
+namespace {
+
+using lora::SliceTable;
+
+constexpr int64_t kMaxI32 = 0x7fffffff;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+int vec_elems(int dtype) { return 16 / elem_bytes(dtype); }
+
+lora_status check_common(int dtype, int64_t T, int32_t slots, int32_t R) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || T > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (slots < 1 || slots > 8192) return LORA_ERR_UNSUPPORTED;
+  if (R < 1 || R > 256) return LORA_ERR_UNSUPPORTED;
+  if (R % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  return LORA_OK;
+}
+
+lora_status check_addr(const int32_t* token_order, const int32_t* slot_indptr,
+                       const int32_t* ranks) {
+  if (!token_order || !slot_indptr || !ranks) return LORA_ERR_INVALID_ARG;
+  return LORA_OK;
+}
+
+lora_status make_slices(int dtype, const int64_t* out_slices, int32_t num_slices, int32_t R,
+                        SliceTable* st) {
+  if (num_slices < 1 || num_slices > lora::kMaxSlices) return LORA_ERR_UNSUPPORTED;
+  if (!out_slices) return LORA_ERR_INVALID_ARG;
+  if ((int64_t)num_slices * R > 1024) return LORA_ERR_UNSUPPORTED;
+  int64_t off = 0;
+  st->n = num_slices;
+  st->off[0] = 0;
+  for (int i = 0; i < num_slices; ++i) {
+    const int64_t w = out_slices[i];
+    if (w < 1) return LORA_ERR_INVALID_ARG;
+    if (w % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+    off += w;
+    if (off > (1 << 30)) return LORA_ERR_INVALID_ARG;
+    st->off[i + 1] = (int)off;
+  }
+  return LORA_OK;
+}
+
+lora_status hip_status(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_ERR_HIP; }
+
+size_t ws_h_bytes(int64_t T, int32_t S, int32_t R) {
+  return (((size_t)T * S * R * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_INVALID_ARG: return "invalid argument";
+    case LORA_ERR_UNSUPPORTED: return "unsupported dtype or size";
+    case LORA_ERR_ALIGNMENT: return "pointer or row width not 16-byte aligned";
+    case LORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LORA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
+
+lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t slots,
+                                  int32_t* token_order, int32_t* slot_indptr, void* stream) {
+  if (T < 0 || T > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (slots < 1 || slots > 8192) return LORA_ERR_UNSUPPORTED;
+  if (!slot_indptr) return LORA_ERR_INVALID_ARG;
+  if (T > 0 && (!token_slot || !token_order)) return LORA_ERR_INVALID_ARG;
+  return hip_status(lora::launch_build_addressing(token_slot, (int)T, slots, token_order,
+                                                  slot_indptr, (hipStream_t)stream));
+}
+
+lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features, const void* a,
+                        int32_t slots, int32_t num_slices, int32_t R,
+                        const int32_t* token_order, const int32_t* slot_indptr,
+                        const int32_t* ranks, float* h, void* stream) {
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  if (num_slices < 1 || num_slices > lora::kMaxSlices) return LORA_ERR_UNSUPPORTED;
+  if ((int64_t)num_slices * R > 1024) return LORA_ERR_UNSUPPORTED;
+  if (in_features < 1 || in_features > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!x || !a || !h) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(x) || !aligned16(a) || !aligned16(h)) return LORA_ERR_ALIGNMENT;
+  if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  return hip_status(lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices,
+                                        R, token_order, slot_indptr, ranks, h,
+                                        (hipStream_t)stream));
+}
+
+lora_status lora_gather_shrink(int dtype, const int32_t* ids, int64_t T, int64_t vocab,
+                               const void* a, int32_t slots, int32_t R,
+                               const int32_t* token_order, const int32_t* slot_indptr,
+                               const int32_t* ranks, float* h, void* stream) {
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  if (vocab < 1 || vocab > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!ids || !a || !h) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(a) || !aligned16(h)) return LORA_ERR_ALIGNMENT;
+  return hip_status(lora::launch_gather_shrink(dtype, ids, (int)T, vocab, a, slots, R,
+                                               token_order, slot_indptr, ranks, h,
+                                               (hipStream_t)stream));
+}
+
+lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices,
+                        int32_t num_slices, const float* h, const void* b, int32_t slots,
+                        int32_t R, const int32_t* token_order, const int32_t* slot_indptr,
+                        const int32_t* ranks, const float* scalings, void* stream) {
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  SliceTable tab;
+  if ((st = make_slices(dtype, out_slices, num_slices, R, &tab)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;
+  if (!y || !h || !b || !scalings) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(y) || !aligned16(h) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
+  return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
+                                        slot_indptr, ranks, scalings, (hipStream_t)stream));
+}
+
+size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
+                                         int32_t num_slices, int32_t R) {
+  (void)in_features;
+  (void)slots;
+  if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
+      R > 256)
+    return 0;
+  return ws_h_bytes(T, num_slices, R) + 256;
+}
+
+lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int64_t in_features,
+                              const int64_t* out_slices, int32_t num_slices, const void* a,
+                              const void* b, int32_t slots, int32_t R,
+                              const int32_t* token_order, const int32_t* slot_indptr,
+                              const int32_t* ranks, const float* scalings, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  SliceTable tab;
+  if ((st = make_slices(dtype, out_slices, num_slices, R, &tab)) != LORA_OK) return st;
+  if (in_features < 1 || in_features > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!x || !y || !a || !b || !scalings) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(a) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
+  if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  const size_t need = lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R);
+  if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  float* h = static_cast<float*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                     token_order, slot_indptr, ranks, h, s);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
+                                        slot_indptr, ranks, scalings, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Device helpers shared by the LoRA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Element tags: BF16 data is handled as raw 16-bit patterns packed two per
+// 32-bit word; F32 data as floats. Both move in 16-byte vectors.
+struct BF16 {
+  static constexpr int kVec = 8;    // elements per 16-byte vector
+  static constexpr int kBytes = 2;
+};
+struct F32 {
+  static constexpr int kVec = 4;
+  static constexpr int kBytes = 4;
+};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return to_bf16_bits(lo) | (to_bf16_bits(hi) << 16);
+}
+
+// Two-term bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int clamp_rank(int r, int R) { return r < 0 ? 0 : (r > R ? R : r); }
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Exclusive prefix sum across the block; `scratch` holds >= 17 ints of LDS.
+// Every thread of the block must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < nw ? scratch[lane] : 0;
+    int si = wave_inclusive_scan(s);
+    if (lane < nw) scratch[lane] = si - s;
+    if (lane == nw - 1) scratch[16] = si;
+  }
+  __syncthreads();
+  int r = inc - v + scratch[w];
+  if (total) *total = scratch[16];
+  __syncthreads();
+  return r;
+}
+
+// Slot of position p of token_order: the s with slot_indptr[s] <= p <
+// slot_indptr[s+1]; `slots` when p is in the dead region.
+__device__ __forceinline__ int slot_of_position(const int32_t* __restrict__ indptr, int slots,
+                                                int p) {
+  if (p >= indptr[slots]) return slots;
+  int lo = 0, hi = slots;  // invariant: indptr[lo] <= p < indptr[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (indptr[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Segment [beg, beg + n) of slot s in token_order, clamped to [0, T] so a
+// malformed addressing can give wrong values but never an access outside the
+// buffers.
+__device__ __forceinline__ void segment_of(const int32_t* __restrict__ indptr, int s, int T,
+                                           int& beg, int& n) {
+  int b = indptr[s], e = indptr[s + 1];
+  b = min(max(b, 0), T);
+  e = min(max(e, b), T);
+  beg = b;
+  n = e - b;
+}
+
+// Token index read from token_order, clamped into [0, T).
+__device__ __forceinline__ int token_at(const int32_t* __restrict__ order, int p, int T) {
+  const int t = order[p];
+  return min(max(t, 0), T - 1);
+}
+
+// Work-item location: given per-slot item counts count(s), find the slot
+// owning `item` and the item's index inside that slot. Block-cooperative:
+// every thread of the block must call it; the result is uniform.
+struct SlotItem {
+  int slot;   // -1 when item >= total
+  int local;
+};
+
+template <typename CountFn>
+__device__ __forceinline__ SlotItem locate_item(int item, int slots, CountFn count,
+                                                int* scratch /* >= 20 ints LDS */) {
+  const int nthreads = blockDim.x;
+  const int chunk = (slots + nthreads - 1) / nthreads;
+  const int s0 = threadIdx.x * chunk;
+  const int s1 = min(slots, s0 + chunk);
+  int local = 0;
+  for (int s = s0; s < s1; ++s) local += count(s);
+  int total = 0;
+  int excl = block_exclusive_scan(local, scratch, &total);
+  if (threadIdx.x == 0) { scratch[18] = -1; scratch[19] = 0; }
+  __syncthreads();
+  if (item >= excl && item < excl + local) {
+    int run = excl;
+    for (int s = s0; s < s1; ++s) {
+      int c = count(s);
+      if (item < run + c) { scratch[18] = s; scratch[19] = item - run; break; }
+      run += c;
+    }
+  }
+  __syncthreads();
+  SlotItem r{scratch[18], scratch[19]};
+  __syncthreads();
+  return r;
+}
+
+}  // namespace lora

@@ -1,0 +1,177 @@
+/*
+ * lora_mi355x.h: C ABI of the batched multi-LoRA delta for MI355X (gfx950).
+ *
+ * One step of multi-adapter LoRA serving adds, for every token t of a batch,
+ * the low-rank update of the adapter slot the token is routed to:
+ *
+ *   shrink   h[t] = x[t] @ A[slot(t)]^T                  (a gather of A's column
+ *                                                         for an embedding target)
+ *   expand   y[t, slice i] += scaling[slot(t)] * h[t, slice i] @ B[slot(t), slice i]^T
+ *
+ * Source: the mstar.engine.resources.lora.backend page (module overview and
+ * LoraBackend.shrink / gather_shrink / expand_fused / apply_linear_), with
+ * the fused-output layout of mstar.model.components.linear (FusedColumnLinear:
+ * shards along the output dimension, in order).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers unless marked (host). The caller owns every
+ * buffer; the library keeps no pointer past a call and allocates nothing.
+ * Every call only enqueues work on `stream` (a hipStream_t; NULL is the null
+ * stream): no host synchronisation, no device-to-host copy, no allocation, so
+ * every call may be recorded under hipStreamBeginCapture. A return of
+ * LORA_OK means the work was enqueued.
+ *
+ * Layouts (all row-major, contiguous):
+ *   x        [T, in]                 dtype            (linear target)
+ *   ids      [T]                     int32            (embedding target)
+ *   y        [T, out]                dtype, updated in place; out = sum(out_slices)
+ *   a        [slots, S*R, in]        dtype            (S = num_slices; rows i*R..i*R+R-1
+ *                                                      belong to slice i)
+ *   a (emb.) [slots, R, vocab]       dtype
+ *   b        [slots, out, R]         dtype            (rows off_i..off_i+w_i-1 belong to
+ *                                                      slice i, off_i = sum of widths before i)
+ *   h        [T, S*R]                float32
+ *   ranks    [slots]                 int32, clamped to [0, R] on the device
+ *   scalings [slots]                 float32
+ *   token_slot [T]                   int32; a value outside [0, slots) marks a token
+ *                                    with no adapter ("dead")
+ *   token_order [T], slot_indptr [slots+1]: the addressing (see
+ *                                    lora_build_addressing)
+ * dtype is LORA_F32 or LORA_BF16 and applies to x, a, b and y together;
+ * h, scalings and all accumulation are float32.
+ *
+ * What is never read: rows of A at or past a slot's rank, columns of B at or
+ * past it, all of A and B for a rank-0 slot, x rows of dead tokens and of
+ * rank-0 slots. Results never depend on those values (NaN there is harmless).
+ *
+ * Invalid device DATA never traps: a slot outside [0, slots) is a dead token,
+ * an id outside [0, vocab) contributes nothing, a rank is clamped to [0, R].
+ * Invalid HOST arguments return an error before anything is enqueued.
+ *
+ * Limits checked on the host: 1 <= slots <= 8192, 1 <= R <= 256,
+ * 1 <= num_slices <= 8, S*R <= 1024, 0 <= T < 2^31, 1 <= in < 2^31.
+ * Alignment: x, a, b, y, h must be 16-byte aligned; `in` (linear targets),
+ * R and every out_slices width must be multiples of 8 elements for bf16 and
+ * of 4 for f32 (so every row starts on a 16-byte boundary).
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_INVALID_ARG = 1, /* null pointer with work to do, negative or out-of-range size */
+  LORA_ERR_UNSUPPORTED = 2, /* dtype, R, num_slices or slots outside the supported set */
+  LORA_ERR_ALIGNMENT = 3,   /* a pointer or a row width breaks the 16-byte rule above */
+  LORA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  LORA_ERR_HIP = 5          /* a kernel launch failed (hipGetLastError after launch) */
+} lora_status;
+
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* lora_status_string(int status);
+
+/* Version string of the library build (static string). */
+const char* lora_version(void);
+
+/*
+ * lora_build_addressing: group the batch's tokens by adapter slot.
+ *
+ * Source: lora.backend module overview (both kernels read the step's
+ * LoraAddressing, never a model-side index, so eager and captured paths
+ * address slots alike) and shrink_reference / expand_reference_, which take
+ * token_order and slot_indptr.
+ *
+ * Output: token_order is a permutation of [0, T). For each slot s the
+ * segment token_order[slot_indptr[s] .. slot_indptr[s+1]) holds the tokens
+ * with token_slot == s in ascending token index (stable); dead tokens follow
+ * slot_indptr[slots], ascending. slot_indptr[0] = 0 and slot_indptr[slots] is
+ * the number of live tokens. Deterministic and bit-exact.
+ * token_slot [T] (read), token_order [T], slot_indptr [slots+1] (written).
+ * T == 0 writes slot_indptr = 0 and nothing else.
+ */
+lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t slots,
+                                  int32_t* token_order, int32_t* slot_indptr,
+                                  void* stream);
+
+/*
+ * lora_shrink: h[t, i*R + j] = x[t] . a[slot(t), i*R + j] for j < rank(slot(t)).
+ *
+ * Source: lora.backend, LoraBackend.shrink (h[t] = x[t] @ a[slot(t)]^T) and
+ * shrink_reference (zeros where the expand does not read).
+ * Writes ALL of h [T, num_slices*R]: every entry the expand does not read
+ * (dead tokens, rank-0 slots, columns at or past a slot's rank) is 0.
+ * Segments long enough to form a dense contraction run on bf16 MFMA, short
+ * ones on a VALU dot-product path; the choice is made on the device.
+ */
+lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features,
+                        const void* a, int32_t slots, int32_t num_slices, int32_t R,
+                        const int32_t* token_order, const int32_t* slot_indptr,
+                        const int32_t* ranks, float* h, void* stream);
+
+/*
+ * lora_gather_shrink: h[t, j] = a[slot(t), j, ids[t]] for j < rank(slot(t)).
+ *
+ * Source: lora.backend, LoraBackend.gather_shrink (the shrink of a token's
+ * one-hot is A's column for it; an id outside [0, in) contributes nothing)
+ * and gather_shrink_reference. An embedding has one output, so S = 1 and h is
+ * [T, R]. Every other entry of h (dead tokens, invalid ids, j >= rank) is 0.
+ * Bit-exact: each entry is a widened copy of one element of a.
+ */
+lora_status lora_gather_shrink(int dtype, const int32_t* ids, int64_t T, int64_t vocab,
+                               const void* a, int32_t slots, int32_t R,
+                               const int32_t* token_order, const int32_t* slot_indptr,
+                               const int32_t* ranks, float* h, void* stream);
+
+/*
+ * lora_expand: y[t, off_i + o] += scalings[slot(t)] *
+ *              sum_{j < rank} h[t, i*R + j] * b[slot(t), off_i + o, j].
+ *
+ * Source: lora.backend, LoraBackend.expand_fused and expand_reference_; the
+ * slice offsets follow FusedColumnLinear's shard layout.
+ * out_slices (host) [num_slices]: the widths. y is updated in place with one
+ * rounding per element (float32 accumulate, then round-to-nearest-even to
+ * bf16 for bf16 y). Rows of dead tokens and of rank-0 slots are not touched;
+ * columns of h and b at or past a slot's rank are not read.
+ */
+lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices,
+                        int32_t num_slices, const float* h, const void* b, int32_t slots,
+                        int32_t R, const int32_t* token_order, const int32_t* slot_indptr,
+                        const int32_t* ranks, const float* scalings, void* stream);
+
+/*
+ * lora_apply_linear: shrink then expand into y for a linear target.
+ *
+ * Source: lora.backend, LoraBackend.apply_linear_ ("a backend may fuse
+ * them"). Same result as lora_shrink followed by lora_expand (h kept in
+ * float32 inside the workspace, never rounded). workspace must be at least
+ * lora_apply_linear_workspace_bytes(...) bytes, 256-byte aligned, and zero-
+ * filled before its FIRST use; every completed call leaves its counters at
+ * zero again, so it can be reused (and replayed from a captured graph)
+ * without clearing. Calls that share one workspace must not overlap in time.
+ */
+lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T,
+                              int64_t in_features, const int64_t* out_slices,
+                              int32_t num_slices, const void* a, const void* b,
+                              int32_t slots, int32_t R, const int32_t* token_order,
+                              const int32_t* slot_indptr, const int32_t* ranks,
+                              const float* scalings, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_apply_linear needs for these sizes (0 on bad input). */
+size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
+                                         int32_t num_slices, int32_t R);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

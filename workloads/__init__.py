@@ -35,9 +35,15 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
     Inputs here are finite Gaussians; NaN/inf are not produced by the draws
     (poison NaNs are written as bit patterns directly)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.ascontiguousarray(a, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 24
+    for k in range(0, u.size, step):
+        c = u[k:k + step]
+        # finite inputs: c + 0x8000 stays below 2^32, so uint32 does not wrap
+        out[k:k + step] = ((c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1)))
+                           >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(np.shape(a))
 
 
 @dataclass
