@@ -6,17 +6,57 @@
 // outside [0, slots)) keyed after every live slot. One workgroup of up to 16
 // waves does the whole batch, with no host round trip, so a serving step can
 // be captured in a hipGraph:
-//   1. wave w owns the contiguous token range [w*per, (w+1)*per) and counts
-//      its keys into its own LDS histogram row;
+//   1. wave w owns the contiguous token range [w*per, (w+1)*per); for every
+//      group of 64 tokens each lane finds the lanes holding the same key with
+//      one ballot per key bit (log2(slots+1) ballots, independent of how many
+//      distinct keys the group has), which gives its rank among equal keys
+//      and the group's count; the group leaders add the counts into the
+//      wave's own LDS histogram row;
 //   2. per key, the rows are turned into per-wave starting offsets and a key
 //      total; a block-wide exclusive scan of the totals gives slot_indptr;
-//   3. each wave walks its range 64 tokens at a time; inside a group, lanes
-//      sharing a key are ranked with ballots, so the order inside a segment is
-//      ascending token index (stable) with no sorting network.
+//   3. each wave walks its groups again: position = the wave's cursor for the
+//      key + the lane's rank, so a segment lists its tokens in ascending
+//      index (stable). Keys and ranks of the first kCache groups stay in
+//      registers between the passes.
 #include "lora_common.h"
 #include "lora_kernels.h"
 
 namespace lora {
+
+namespace {
+
+constexpr int kCache = 8;   // 64-token groups per wave kept in registers
+
+struct GroupMatch {
+  int key;      // -1 for a lane past the range
+  int rank;     // lanes below this one with the same key
+  int count;    // lanes with this key
+  bool leader;  // lowest lane with this key
+};
+
+__device__ __forceinline__ GroupMatch match_group(const int32_t* __restrict__ token_slot, int t,
+                                                  bool valid, int slots, int nbits) {
+  GroupMatch g;
+  int k = -1;
+  if (valid) {
+    const int s = token_slot[t];
+    k = (s >= 0 && s < slots) ? s : slots;
+  }
+  uint64_t eq = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (k >> b) & 1;
+    const uint64_t bal = __ballot(valid && bit);
+    eq &= bit ? bal : ~bal;
+  }
+  const uint64_t below = eq & ((1ull << lane_id()) - 1ull);
+  g.key = k;
+  g.rank = __popcll(below);
+  g.count = __popcll(eq);
+  g.leader = valid && below == 0;
+  return g;
+}
+
+}  // namespace
 
 __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __restrict__ token_slot,
                                                            int T, int slots,
@@ -31,6 +71,7 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = tid / kWave;
+  const int nbits = 32 - __clz(slots);   // bits of the largest key (= slots)
 
   for (int i = tid; i < nw * S1; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
@@ -38,10 +79,20 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   const int per = (T + nw - 1) / nw;
   const int t0 = min(T, w * per);
   const int t1 = min(T, t0 + per);
-  for (int t = t0 + lane; t < t1; t += kWave) {
-    int s = token_slot[t];
-    int k = (s >= 0 && s < slots) ? s : slots;
-    atomicAdd(&cnt[w * S1 + k], 1);
+  int* row = cnt + w * S1;
+  GroupMatch cache[kCache];
+#pragma unroll
+  for (int c = 0; c < kCache; ++c) cache[c] = GroupMatch{-1, 0, 0, false};
+  {
+    int c = 0;
+    for (int base = t0; base < t1; base += kWave, ++c) {
+      const int t = base + lane;
+      const GroupMatch g = match_group(token_slot, t, t < t1, slots, nbits);
+      if (g.leader) row[g.key] += g.count;   // distinct keys: no two leaders collide
+#pragma unroll
+      for (int cc = 0; cc < kCache; ++cc)
+        if (cc == c) cache[cc] = g;
+    }
   }
   __syncthreads();
 
@@ -77,30 +128,24 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   }
   __syncthreads();
 
-  // stable scatter: only wave w touches row w of cnt, so no atomics here
-  int* cur = cnt + w * S1;
-  for (int base = t0; base < t1; base += kWave) {
-    const int t = base + lane;
-    const bool valid = t < t1;
-    int k = -1;
-    if (valid) {
-      int s = token_slot[t];
-      k = (s >= 0 && s < slots) ? s : slots;
-    }
-    uint64_t active = __ballot(valid);
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int kl = __shfl(k, leader);
-      const uint64_t m = __ballot(valid && k == kl) & active;
-      int pos0 = 0;
-      if (lane == leader) pos0 = cur[kl];
-      pos0 = __shfl(pos0, leader);
-      if ((m >> lane) & 1ull) {
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        token_order[pos0 + rank] = t;
+  // stable scatter: only wave w touches row w of cnt
+  {
+    int c = 0;
+    for (int base = t0; base < t1; base += kWave, ++c) {
+      const int t = base + lane;
+      GroupMatch g;
+      if (c < kCache) {
+#pragma unroll
+        for (int cc = 0; cc < kCache; ++cc)
+          if (cc == c) g = cache[cc];
+      } else {
+        g = match_group(token_slot, t, t < t1, slots, nbits);
       }
-      if (lane == leader) cur[kl] = pos0 + __popcll(m);
-      active &= ~m;
+      int pos = 0;
+      if (t < t1) pos = row[g.key] + g.rank;
+      __builtin_amdgcn_wave_barrier();
+      if (g.leader) row[g.key] += g.count;
+      if (t < t1) token_order[pos] = t;
     }
   }
 }

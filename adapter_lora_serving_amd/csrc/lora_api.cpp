@@ -140,12 +140,14 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
 
 size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
                                          int32_t num_slices, int32_t R) {
-  (void)in_features;
-  (void)slots;
   if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
-      R > 256)
+      R > 256 || slots < 1 || slots > 8192 || in_features < 1 || in_features > kMaxI32)
     return 0;
-  return ws_h_bytes(T, num_slices, R) + 256;
+  // counters, then the larger body: the fused path's partial tiles or the
+  // shrink-then-expand path's h
+  const size_t fused = lora::fused_partial_bytes(slots, num_slices, R, (int)in_features);
+  const size_t split = ws_h_bytes(T, num_slices, R);
+  return lora::counter_bytes(slots, num_slices) + (fused > split ? fused : split);
 }
 
 lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int64_t in_features,
@@ -167,8 +169,13 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
   const size_t need = lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R);
   if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
-  float* h = static_cast<float*>(workspace);
   hipStream_t s = (hipStream_t)stream;
+  if (lora::fused_supported(dtype, tab, R, (int)T, (int)in_features))
+    return hip_status(lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots,
+                                               R, token_order, slot_indptr, ranks, scalings,
+                                               workspace, s));
+  float* h = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      lora::counter_bytes(slots, num_slices));
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
                                      token_order, slot_indptr, ranks, h, s);
   if (e != hipSuccess) return LORA_ERR_HIP;

@@ -18,6 +18,18 @@ struct SliceTable {
   int off[kMaxSlices + 1];
 };
 
+// Column chunks of the fused output handed to decode work items: chunk k
+// covers columns [c0[k], c1[k]) of slice slice[k].
+constexpr int kMaxChunks = 64;
+struct ChunkTable {
+  int n;
+  int per_slice[kMaxSlices];   // chunks of each slice
+  int first[kMaxSlices];       // index of each slice's first chunk
+  int slice[kMaxChunks];
+  int c0[kMaxChunks];
+  int c1[kMaxChunks];
+};
+
 hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
                                    int32_t* token_order, int32_t* slot_indptr,
                                    hipStream_t stream);
@@ -35,5 +47,22 @@ hipError_t launch_expand(int dtype, void* y, int T, const SliceTable& st, const 
                          const void* b, int slots, int R, const int32_t* token_order,
                          const int32_t* indptr, const int32_t* ranks, const float* scalings,
                          hipStream_t stream);
+
+// Fused shrink + expand (bf16, MFMA). fused_supported() tells whether the
+// shapes qualify (bf16, every slice width a multiple of 16, R <= 256, every
+// buffer below 2 GiB).
+bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in);
+// Workspace layout of lora_apply_linear: [counters | body]. The counters (a
+// {count, base} int pair per (slot, chunk index), a fixed 4 MiB region) are
+// used only by the fused kernel and stay consistent across calls of any
+// shape. The body holds the fused path's fp32 partial h tiles or the other
+// path's h.
+size_t counter_bytes(int slots, int S);
+size_t fused_partial_bytes(int slots, int S, int R, int in);
+hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const SliceTable& st,
+                              const void* a, const void* b, int slots, int R,
+                              const int32_t* token_order, const int32_t* indptr,
+                              const int32_t* ranks, const float* scalings, void* workspace,
+                              hipStream_t stream);
 
 }  // namespace lora

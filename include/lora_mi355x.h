@@ -154,9 +154,12 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
  * them"). Same result as lora_shrink followed by lora_expand (h kept in
  * float32 inside the workspace, never rounded). workspace must be at least
  * lora_apply_linear_workspace_bytes(...) bytes, 256-byte aligned, and zero-
- * filled before its FIRST use; every completed call leaves its counters at
- * zero again, so it can be reused (and replayed from a captured graph)
- * without clearing. Calls that share one workspace must not overlap in time.
+ * filled before its FIRST use. Its first 4 MiB hold synchronisation
+ * counters that stay consistent from call to call, so one workspace can be
+ * reused across calls of any shape (and replayed from a captured graph)
+ * without clearing; clearing it again between calls is also allowed. Calls
+ * that share one workspace must not overlap in time (one workspace per
+ * stream).
  */
 lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T,
                               int64_t in_features, const int64_t* out_slices,

@@ -293,6 +293,46 @@ def test_run_to_run_deterministic(k):
     assert torch().equal(h1, h2) and torch().equal(y1, y2) and torch().equal(y3, y4)
 
 
+@pytest.mark.parametrize("k", [2, 5])
+def test_decode_wait_fallback(k, monkeypatch):
+    """With the producer wait bound at zero every expand piece computes its
+    slice's h itself; the result must still match the oracle."""
+    monkeypatch.setenv("LORA_SPIN_LIMIT", "0")
+    wl = W.make_config(k, 1, **SMALL[k])
+    tg = wl.targets[0]
+    _, _, y = GpuTarget(wl, tg).run(fused=True)
+    _, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, "fallback")
+
+
+def test_workspace_counters_consistent():
+    """After every call each {count, base} pair of the fused path's counter
+    region is equal again (graph replays and later calls rely on it), also
+    across calls of different shapes sharing one workspace."""
+    t = torch()
+    ws = None
+    for k in (2, 5, 2):
+        wl = W.make_config(k, 0, **SMALL[k])
+        tg = wl.targets[0]
+        g = GpuTarget(wl, tg)
+        need = L.workspace_bytes(wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R)
+        if ws is None or ws.numel() < need:
+            old = ws
+            ws = t.zeros(max(need, 1 << 23), dtype=t.uint8, device="cuda:0")
+            if old is not None:
+                ws[: old.numel()].copy_(old)
+        addr = g.addressing()
+        for _ in range(2):
+            y = g.y0.clone()
+            L.apply_linear_(g.x, y, g.a, g.b, addr, g.ranks, g.scal, tg.out_slices, workspace=ws)
+        t.cuda.synchronize()
+        _, y_ref = O.run_target(wl, tg)
+        assert_tol(f64(y), y_ref, f"shared workspace config {k}")
+        pairs = ws[: 8192 * 64 * 8].view(t.int32).view(-1, 2)
+        assert bool((pairs[:, 0] == pairs[:, 1]).all())
+        assert int(pairs[:, 0].abs().sum()) > 0       # the counters were used
+
+
 def test_guard_bands():
     """Nothing is written outside y's rows or h's rows."""
     t = torch()
