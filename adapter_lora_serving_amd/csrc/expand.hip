@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kBlock) void k_expand_valu(void* __restrict__ y_, i
                                                         int R, const int32_t* __restrict__ token_order,
                                                         const int32_t* __restrict__ indptr,
                                                         const int32_t* __restrict__ ranks,
-                                                        const float* __restrict__ scalings) {
+                                                        const float* __restrict__ scalings,
+                                                        int max_seg) {
   __shared__ int scratch[24];
   extern __shared__ float hl[];  // [kTG][S*R]
   const int S = st.n;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void k_expand_valu(void* __restrict__ y_, i
     int b0, n;
     segment_of(indptr, s, T, b0, n);
     const int r = clamp_rank(ranks[s], R);
-    return (n > 0 && r > 0) ? nchunk * ((n + kTG - 1) / kTG) : 0;
+    return (n > 0 && n <= max_seg && r > 0) ? nchunk * ((n + kTG - 1) / kTG) : 0;
   };
   const SlotItem it = locate_item(blockIdx.x, slots, count, scratch);
   if (it.slot < 0) return;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void k_expand_valu(void* __restrict__ y_, i
 hipError_t launch_expand(int dtype, void* y, int T, const SliceTable& st, const float* h,
                          const void* b, int slots, int R, const int32_t* token_order,
                          const int32_t* indptr, const int32_t* ranks, const float* scalings,
-                         hipStream_t stream) {
+                         int max_seg, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int out = st.off[st.n];
   const int cols = kBlock * (dtype == kDtypeBF16 ? BF16::kVec : F32::kVec);
@@ -160,10 +161,10 @@ hipError_t launch_expand(int dtype, void* y, int T, const SliceTable& st, const 
   const size_t lds = (size_t)kTG * st.n * R * sizeof(float);
   if (dtype == kDtypeBF16)
     hipLaunchKernelGGL(k_expand_valu<BF16>, dim3((unsigned)grid), dim3(kBlock), lds, stream, y, T,
-                       st, h, b, slots, R, token_order, indptr, ranks, scalings);
+                       st, h, b, slots, R, token_order, indptr, ranks, scalings, max_seg);
   else
     hipLaunchKernelGGL(k_expand_valu<F32>, dim3((unsigned)grid), dim3(kBlock), lds, stream, y, T, st,
-                       h, b, slots, R, token_order, indptr, ranks, scalings);
+                       h, b, slots, R, token_order, indptr, ranks, scalings, max_seg);
   return hipGetLastError();
 }
 

@@ -586,7 +586,9 @@ int decode_chunk_cols(int R) {
 }
 
 int k_parts(int in) {
-  int kp = in / 2048;
+  // K parts of a decode shrink (each ~2048 deep); overridable for tuning
+  const int env = env_int("LORA_KPARTS", 0);
+  int kp = env > 0 ? env : in / 2048;
   return kp < 1 ? 1 : kp > 8 ? 8 : kp;
 }
 
@@ -624,7 +626,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              hipStream_t stream) {
+                              bool with_long, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // expand chunks: each slice cut into pieces of at most `cols` columns
   // (a multiple of 16), at most kMaxChunks in all
@@ -655,7 +657,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
   const int64_t n_shrink = slots8 * st.n * KP;
   const int64_t n_expand = slots8 * ct.n;
-  const int64_t n_prefill = (T + kMT - 1) / kMT + slots;
+  const int64_t n_prefill = with_long ? (T + kMT - 1) / kMT + slots : 0;
   const int64_t grid = n_shrink + n_expand + n_prefill;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   int2* pairs = (int2*)workspace;

@@ -59,6 +59,13 @@ size_t ws_h_bytes(int64_t T, int32_t S, int32_t R) {
   return (((size_t)T * S * R * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+size_t partial_bytes(int32_t slots, int32_t S, int32_t R, int64_t in) {
+  return (lora::fused_partial_bytes(slots, S, R, (int)in) + 255) & ~(size_t)255;
+}
+
+// Batches smaller than this run every segment in the fused kernel.
+constexpr int64_t kFusedAllBelowT = 1024;
+
 }  // namespace
 
 extern "C" {
@@ -101,9 +108,21 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(x) || !aligned16(a) || !aligned16(h)) return LORA_ERR_ALIGNMENT;
   if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
-  return hip_status(lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices,
-                                        R, token_order, slot_indptr, ranks, h,
-                                        (hipStream_t)stream));
+  // per-segment choice on the device: the VALU kernel takes segments of at
+  // most kLongSegment tokens, the MFMA kernel the longer ones
+  SliceTable none;
+  none.n = 1;
+  none.off[0] = 0;
+  none.off[1] = 16;
+  const bool mfma = lora::sgmv_supported(dtype, none, R, (int)T, (int)in_features);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                     token_order, slot_indptr, ranks, h,
+                                     mfma ? lora::kLongSegment : lora::kNoMaxSeg, s);
+  if (e == hipSuccess && mfma)
+    e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                 token_order, slot_indptr, ranks, h, nullptr, 1, s);
+  return hip_status(e);
 }
 
 lora_status lora_gather_shrink(int dtype, const int32_t* ids, int64_t T, int64_t vocab,
@@ -134,8 +153,15 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
   if (!y || !h || !b || !scalings) return LORA_ERR_INVALID_ARG;
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(y) || !aligned16(h) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
-  return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
-                                        slot_indptr, ranks, scalings, (hipStream_t)stream));
+  const bool mfma = lora::sgmv_supported(dtype, tab, R, (int)T, 8);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
+                                     slot_indptr, ranks, scalings,
+                                     mfma ? lora::kLongSegment : lora::kNoMaxSeg, s);
+  if (e == hipSuccess && mfma)
+    e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr, ranks,
+                                 scalings, s);
+  return hip_status(e);
 }
 
 size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
@@ -143,11 +169,11 @@ size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t
   if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
       R > 256 || slots < 1 || slots > 8192 || in_features < 1 || in_features > kMaxI32)
     return 0;
-  // counters, then the larger body: the fused path's partial tiles or the
-  // shrink-then-expand path's h
-  const size_t fused = lora::fused_partial_bytes(slots, num_slices, R, (int)in_features);
-  const size_t split = ws_h_bytes(T, num_slices, R);
-  return lora::counter_bytes(slots, num_slices) + (fused > split ? fused : split);
+  // counters, the fused path's partial tiles, then h for the long segments
+  // (or for the whole batch on the shrink-then-expand path)
+  // and the K parts of the SGMV shrink
+  return lora::counter_bytes(slots, num_slices) + partial_bytes(slots, num_slices, R, in_features) +
+         ws_h_bytes(T, num_slices, R) * (1 + lora::sgmv_kparts((int)in_features));
 }
 
 lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int64_t in_features,
@@ -170,17 +196,35 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
   if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
   hipStream_t s = (hipStream_t)stream;
-  if (lora::fused_supported(dtype, tab, R, (int)T, (int)in_features))
-    return hip_status(lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots,
-                                               R, token_order, slot_indptr, ranks, scalings,
-                                               workspace, s));
   float* h = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      lora::counter_bytes(slots, num_slices));
+                                      lora::counter_bytes(slots, num_slices) +
+                                      partial_bytes(slots, num_slices, R, in_features));
+  if (lora::fused_supported(dtype, tab, R, (int)T, (int)in_features)) {
+    // The host picks the kernel family from T only (fixed per captured
+    // graph): small batches run everything in the fused kernel; larger ones
+    // leave segments longer than 16 tokens to the SGMV shrink and expand,
+    // which write and read their h in the workspace. Which segment goes
+    // where is decided on the device from slot_indptr.
+    const bool small = T < kFusedAllBelowT;
+    hipError_t e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
+                                            token_order, slot_indptr, ranks, scalings, workspace,
+                                            small, s);
+    if (e == hipSuccess && !small) {
+      const int kp = lora::sgmv_kparts((int)in_features);
+      float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);
+      e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                   token_order, slot_indptr, ranks, h, parts, kp, s);
+    }
+    if (e == hipSuccess && !small)
+      e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                   ranks, scalings, s);
+    return hip_status(e);
+  }
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                     token_order, slot_indptr, ranks, h, s);
+                                     token_order, slot_indptr, ranks, h, lora::kNoMaxSeg, s);
   if (e != hipSuccess) return LORA_ERR_HIP;
   return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
-                                        slot_indptr, ranks, scalings, s));
+                                        slot_indptr, ranks, scalings, lora::kNoMaxSeg, s));
 }
 
 }  // extern "C"

@@ -118,6 +118,7 @@ __device__ __forceinline__ int token_at(const int32_t* __restrict__ order, int p
 struct SlotItem {
   int slot;   // -1 when item >= total
   int local;
+  int total;  // items over all slots
 };
 
 template <typename CountFn>
@@ -142,7 +143,7 @@ __device__ __forceinline__ SlotItem locate_item(int item, int slots, CountFn cou
     }
   }
   __syncthreads();
-  SlotItem r{scratch[18], scratch[19]};
+  SlotItem r{scratch[18], scratch[19], total};
   __syncthreads();
   return r;
 }

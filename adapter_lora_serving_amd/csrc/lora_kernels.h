@@ -39,14 +39,31 @@ hipError_t launch_gather_shrink(int dtype, const int32_t* ids, int T, int64_t vo
                                 const int32_t* indptr, const int32_t* ranks, float* h,
                                 hipStream_t stream);
 
+// VALU (BGMV) shrink / expand; segments longer than max_seg are skipped
+// (the SGMV kernels take them).
+constexpr int kNoMaxSeg = 0x7fffffff;
 hipError_t launch_shrink(int dtype, const void* x, int T, int in, const void* a, int slots,
                          int S, int R, const int32_t* token_order, const int32_t* indptr,
-                         const int32_t* ranks, float* h, hipStream_t stream);
+                         const int32_t* ranks, float* h, int max_seg, hipStream_t stream);
 
 hipError_t launch_expand(int dtype, void* y, int T, const SliceTable& st, const float* h,
                          const void* b, int slots, int R, const int32_t* token_order,
                          const int32_t* indptr, const int32_t* ranks, const float* scalings,
-                         hipStream_t stream);
+                         int max_seg, hipStream_t stream);
+
+// SGMV (bf16 MFMA) shrink / expand over segments longer than kLongSegment.
+constexpr int kLongSegment = 16;
+bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in);
+// kparts > 1 splits K: the parts go to `parts` (kparts * T * S * R floats)
+// and are summed into h in part order.
+int sgmv_kparts(int in);
+hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
+                              int R, const int32_t* order, const int32_t* indptr,
+                              const int32_t* ranks, float* h, float* parts, int kparts,
+                              hipStream_t stream);
+hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float* h, const void* b,
+                              int slots, int R, const int32_t* order, const int32_t* indptr,
+                              const int32_t* ranks, const float* scalings, hipStream_t stream);
 
 // Fused shrink + expand (bf16, MFMA). fused_supported() tells whether the
 // shapes qualify (bf16, every slice width a multiple of 16, R <= 256, every
@@ -59,10 +76,12 @@ bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in);
 // path's h.
 size_t counter_bytes(int slots, int S);
 size_t fused_partial_bytes(int slots, int S, int R, int in);
+// with_long: the fused kernel also takes segments longer than 16 tokens
+// (16-token blocks over every column); otherwise it leaves them to SGMV.
 hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const SliceTable& st,
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              hipStream_t stream);
+                              bool with_long, hipStream_t stream);
 
 }  // namespace lora

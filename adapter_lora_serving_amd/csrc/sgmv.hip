@@ -1,0 +1,494 @@
+// Segment-tiled (SGMV) shrink and expand on bf16 MFMA, for slot segments
+// longer than 16 tokens, where the per-slot products are real dense
+// contractions.
+//
+// Follows the mstar lora.backend page: LoraBackend.shrink (h[t] =
+// x[t] @ a[slot(t)]^T) and LoraBackend.expand_fused (y[t, slice i] +=
+// scalings[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T); the slice
+// layout follows mstar.model.components.linear, FusedColumnLinear.
+//
+// Shrink item: (slot, block of 32 tokens of its segment, slice). Four waves:
+//   wave w computes token tile (w & 1) against rank tiles of half (w >> 1).
+//   K advances in chunks of 64: the x block [32 x 64] and A rows [RP x 64]
+//   are staged in LDS (double buffered, rows padded by 16 bytes so the
+//   MFMA operand reads hit distinct banks) with one 16-byte buffer load per
+//   thread and piece; rows of A at or past the rank lie outside the A
+//   resource and read as zeros without a memory access. Each wave writes its
+//   16 x 16 tiles of h (fp32) directly: no reduction across waves.
+// Expand item: (slot, block of 64 tokens, 256 output columns of one slice).
+//   The block's h rows are scaled and split into bf16 hi + lo in LDS; every
+//   wave prefetches its 4 column tiles of B and y in one round trip, then
+//   y^T tile = B_tile . H^T with two v_mfma_f32_16x16x16_bf16 per 16 ranks
+//   and 4 token tiles, one rounding of y.
+// Items are numbered XCD by XCD (block b runs on XCD b % 8 and takes item
+// (b % 8) * ceil(N/8) + b / 8), so consecutive blocks of one slot share an
+// XCD's L2 for A (shrink) or B (expand).
+#include "lora_common.h"
+#include "lora_kernels.h"
+
+namespace lora {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLong = 16;     // segments longer than this take the SGMV path
+constexpr int kBMe = 64;      // tokens per expand item
+constexpr int kCC = 256;      // output columns per expand item
+constexpr int kKC = 64;       // K elements per staged chunk
+constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
+
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// XCD-contiguous item index of block b among n items; -1 past the end.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  const int per = (n + 7) / 8;
+  const int k = b >> 3;
+  if (k >= per) return -1;
+  const int it = (b & 7) * per + k;
+  return it < n ? it : -1;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// shrink
+// ---------------------------------------------------------------------------
+// Item: (slot, block of 128 tokens, slice, K part). Eight waves, wave w owns
+// token tile w (16 tokens) against every rank tile, so its x rows are its own
+// (read straight into registers, D chunks ahead) and only A is shared: A's
+// chunk [RP x 64] goes through a register ring D chunks ahead into a
+// double-buffered LDS tile. A is thus re-read from L2 once per 128 tokens.
+// With kparts > 1 each item writes its partial h to its own buffer
+// (hout + kp * part_stride); k_sum_parts adds them in kp order.
+constexpr int kBMs = 128;
+constexpr int kD = 4;
+
+template <int RT>
+__global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_, int T, int in,
+                                                     const void* __restrict__ a_, int slots, int S,
+                                                     int R, const int32_t* __restrict__ order,
+                                                     const int32_t* __restrict__ indptr,
+                                                     const int32_t* __restrict__ ranks,
+                                                     float* __restrict__ hout, int kparts,
+                                                     int64_t part_stride) {
+  constexpr int RP = RT * 16;
+  constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
+  constexpr int D = RT >= 8 ? 2 : kD;          // chunks in flight (register budget)
+  __shared__ int scratch[24];
+  __shared__ int tok[kBMs];
+  __shared__ __attribute__((aligned(16))) char as[2][RP * kRowB];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  auto count = [&](int s) -> int {
+    int b0, n;
+    segment_of(indptr, s, T, b0, n);
+    return (n > kLong && clamp_rank(ranks[s], R) > 0) ? S * kparts * ((n + kBMs - 1) / kBMs)
+                                                      : 0;
+  };
+  const int total = locate_item(0x7fffffff, slots, count, scratch).total;
+  const int item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  const SlotItem it = locate_item(item, slots, count, scratch);
+  const int s = it.slot;
+  int seg0, n;
+  segment_of(indptr, s, T, seg0, n);
+  const int r = clamp_rank(ranks[s], R);
+  const int nmb = (n + kBMs - 1) / kBMs;
+  const int mb = it.local % nmb;
+  const int rest = it.local / nmb;
+  const int kp = rest % kparts;
+  const int i = rest / kparts;
+  const int ntok = min(kBMs, n - mb * kBMs);
+  if (tid < kBMs) tok[tid] = tid < ntok ? token_at(order, seg0 + mb * kBMs + tid, T) : -1;
+  __syncthreads();
+
+  const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
+  const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S * R + (int64_t)i * R) * in * 2,
+                               (uint32_t)r * (uint32_t)in * 2u);
+  const uint32_t rowG = (uint32_t)in * 2u;
+  const int nchT = (in + kKC - 1) / kKC;
+  const int cbeg = (int)((int64_t)nchT * kp / kparts);
+  const int cend = (int)((int64_t)nchT * (kp + 1) / kparts);
+  const int nch = cend - cbeg;
+
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const int t = tok[w * 16 + m];
+  const uint32_t xrow = t >= 0 ? (uint32_t)t * rowG : kOOB;
+  const int arow = tid >> 3;        // 0..63 (+64 per extra piece)
+  const int apc = tid & 7;
+
+  u32x4 xr[D][2];
+  u32x4 ar[D][AL];
+  auto issue = [&](int slot, int c) {   // loads of chunk c (relative) into ring slot
+    const bool cv = c < nch;
+    const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t e = (uint32_t)((cbeg + c) * kKC + ks * 32 + kg * 8);
+      xr[slot][ks] = bload16(x_r, (cv && xrow != kOOB && e < (uint32_t)in)
+                                      ? xrow + kb + (uint32_t)(ks * 32 + kg * 8) * 2u
+                                      : kOOB);
+    }
+#pragma unroll
+    for (int q = 0; q < AL; ++q) {
+      const int row = arow + 64 * q;
+      const uint32_t e = (uint32_t)((cbeg + c) * kKC + apc * 8);
+      ar[slot][q] = bload16(a_r, (cv && row < RP && e < (uint32_t)in)
+                                     ? (uint32_t)row * rowG + kb + apc * 16u
+                                     : kOOB);
+    }
+  };
+  auto stage = [&](int slot, int buf) {   // A chunk in ring slot -> LDS buffer
+#pragma unroll
+    for (int q = 0; q < AL; ++q) {
+      const int row = arow + 64 * q;
+      if (row < RP) *(u32x4*)(as[buf] + row * kRowB + apc * 16) = ar[slot][q];
+    }
+  };
+
+  const int ntr = (r + 15) / 16;   // rank tiles holding rows below r
+  f32x4 acc[RT];
+#pragma unroll
+  for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);
+  stage(0, 0);
+  __syncthreads();
+#pragma unroll 1
+  for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int c = c0 + d;
+      if (c < nch) {
+        if (c + 1 < nch) stage((d + 1) % D, (c + 1) & 1);
+        const char* ab = as[c & 1];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[d][ks]);
+#pragma unroll
+          for (int nt = 0; nt < RT; ++nt) {
+            if (nt >= ntr) break;   // rank tiles past r hold only zeros
+            const bf16x8 av = __builtin_bit_cast(
+                bf16x8, *(const u32x4*)(ab + (nt * 16 + m) * kRowB + (ks * 32 + kg * 8) * 2));
+            acc[nt] = mfma_k32(xa, av, acc[nt]);
+          }
+        }
+        issue(d, c + D);
+        __syncthreads();
+      }
+    }
+  }
+
+  // lane (m, kg) holds h[token w*16 + 4kg + ii][rank nt*16 + m]
+  const int SR = S * R;
+  float* hp = hout + (int64_t)kp * part_stride;
+#pragma unroll
+  for (int nt = 0; nt < RT; ++nt) {
+    const int j = nt * 16 + m;
+    if (j < R) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int tt = tok[w * 16 + 4 * kg + ii];
+        if (tt >= 0) hp[(int64_t)tt * SR + i * R + j] = acc[nt][ii];
+      }
+    }
+  }
+}
+
+// h[t, :] = sum over kp (in order) of part[kp][t, :], for the tokens of
+// segments longer than kLong (the only rows the parts hold).
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int kparts,
+                                                   int64_t part_stride, float* __restrict__ h,
+                                                   int T, int SR, int slots, int R,
+                                                   const int32_t* __restrict__ order,
+                                                   const int32_t* __restrict__ indptr,
+                                                   const int32_t* __restrict__ ranks) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (position, 4 columns)
+  const int cq = SR / 4;
+  if (g >= (int64_t)T * cq) return;
+  const int p = (int)(g / cq);
+  const int c = (int)(g - (int64_t)p * cq) * 4;
+  const int s = slot_of_position(indptr, slots, p);
+  if (s >= slots) return;
+  int b0, n;
+  segment_of(indptr, s, T, b0, n);
+  if (n <= kLong || clamp_rank(ranks[s], R) == 0) return;
+  const int64_t off = (int64_t)token_at(order, p, T) * SR + c;
+  f32x4 v = *(const f32x4*)(part + off);
+  for (int k = 1; k < kparts; ++k) {
+    const f32x4 u = *(const f32x4*)(part + (int64_t)k * part_stride + off);
+    v = f32x4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
+  }
+  *(f32x4*)(h + off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// expand
+// ---------------------------------------------------------------------------
+// Item: (slot, block of 64 tokens, 256 output columns of one slice). Wave w
+// owns columns [lo + 64w, lo + 64w + 64) for the 64 tokens. The MFMA result
+// comes out as 4 columns of one token per lane; it is staged through a
+// per-wave LDS tile so that y is read and written row-major, 16 bytes per
+// lane: one instruction covers 8 token rows x 128 contiguous bytes, full
+// cache lines, so HBM never sees partial-line writes.
+template <int RT>
+__global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int T, SliceTable st,
+                                                     const float* __restrict__ h,
+                                                     const void* __restrict__ b_, int slots,
+                                                     int R, const int32_t* __restrict__ order,
+                                                     const int32_t* __restrict__ indptr,
+                                                     const int32_t* __restrict__ ranks,
+                                                     const float* __restrict__ scalings) {
+  constexpr int RP = RT * 16;
+  constexpr int RPS = RP + 4;
+  constexpr int MT = kBMe / 16;       // token tiles
+  constexpr int TPW = kCC / 16 / 4;   // column tiles per wave (4: 64 columns)
+  constexpr int SRW = 64 + 4;         // staged row (floats), padded
+  __shared__ int scratch[24];
+  __shared__ int tok[kBMe];
+  __shared__ __attribute__((aligned(16))) uint16_t hhi[kBMe * RPS];
+  __shared__ __attribute__((aligned(16))) uint16_t hlo[kBMe * RPS];
+  __shared__ __attribute__((aligned(16))) float stage[4][16 * SRW];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int S = st.n;
+  const int out = st.off[S];
+  // column chunks: slice i holds ceil(w_i / kCC) chunks
+  int nck = 0;
+  for (int i = 0; i < S; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
+  auto count = [&](int s) -> int {
+    int b0, n;
+    segment_of(indptr, s, T, b0, n);
+    return (n > kLong && clamp_rank(ranks[s], R) > 0) ? nck * ((n + kBMe - 1) / kBMe) : 0;
+  };
+  const int total = locate_item(0x7fffffff, slots, count, scratch).total;
+  const int item = xcd_item(blockIdx.x, total);
+  if (item < 0) return;
+  const SlotItem it = locate_item(item, slots, count, scratch);
+  const int s = it.slot;
+  int seg0, n;
+  segment_of(indptr, s, T, seg0, n);
+  const int r = clamp_rank(ranks[s], R);
+  const int nmb = (n + kBMe - 1) / kBMe;
+  const int mb = it.local % nmb;
+  int ck = it.local / nmb;
+  int i = 0;
+  for (; i < S; ++i) {
+    const int c = (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
+    if (ck < c) break;
+    ck -= c;
+  }
+  const int lo = st.off[i] + ck * kCC;
+  const int hi = min(lo + kCC, st.off[i + 1]);
+  const int ntok = min(kBMe, n - mb * kBMe);
+  if (tid < kBMe) tok[tid] = tid < ntok ? token_at(order, seg0 + mb * kBMe + tid, T) : -1;
+  __syncthreads();
+
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const rsrc_t y_r = make_rsrc(y_, (uint32_t)T * (uint32_t)out * 2u);
+  const rsrc_t b_r = make_rsrc((const char*)b_ + (int64_t)s * out * R * 2,
+                               (uint32_t)out * (uint32_t)R * 2u);
+  const int ntiles = (hi - lo) >> 4;
+  const int cw = lo + w * 64;         // this wave's first column
+  const int ntr = (r + 15) / 16;      // rank tiles holding ranks below r
+
+  // row-major y access: lane -> rows (lane >> 3) and 8 + (lane >> 3) of a
+  // token tile, 16-byte piece (lane & 7) of the wave's 128-byte column span
+  const int prow = lane >> 3;
+  const int ppc = lane & 7;
+  const bool pcol = (w * TPW + (ppc >> 1)) < ntiles;   // piece inside the chunk
+  u32x4 yv[MT][2];
+#pragma unroll
+  for (int q = 0; q < MT; ++q)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int t = tok[q * 16 + prow + 8 * hh];
+      yv[q][hh] = bload16(y_r, (pcol && t >= 0)
+                                   ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
+                                   : kOOB);
+    }
+  s16x4 bv[TPW][RT];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = w * TPW + u;
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      const int kk = ks * 16 + kg * 4;
+      bv[u][ks] = __builtin_bit_cast(
+          s16x4, bload8(b_r, (tile < ntiles && kk < r)
+                                 ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
+                                 : kOOB));
+    }
+  }
+
+  // h rows of the block (only ranks below r are read), scaled, split hi + lo;
+  // all of a thread's loads are issued before any is used
+  const float scale = scalings[s];
+  const int SR = S * R;
+  constexpr int HL = kBMe * RP / 256;   // h values per thread
+  const rsrc_t h_r = make_rsrc(h, (uint32_t)T * (uint32_t)SR * 4u);
+  float hv[HL];
+#pragma unroll
+  for (int k = 0; k < HL; ++k) {
+    const int idx = tid + 256 * k;
+    const int q = idx / RP;
+    const int j = idx - q * RP;
+    const int t = tok[q];
+    hv[k] = __uint_as_float(
+        bload4(h_r, (t >= 0 && j < r) ? ((uint32_t)t * (uint32_t)SR + i * R + j) * 4u : kOOB));
+  }
+#pragma unroll
+  for (int k = 0; k < HL; ++k) {
+    const int idx = tid + 256 * k;
+    const int q = idx / RP;
+    const int j = idx - q * RP;
+    const float v = hv[k] * scale;
+    const uint32_t hb = to_bf16_bits(v);
+    const uint32_t lb = to_bf16_bits(v - __uint_as_float(hb << 16));
+    hhi[q * RPS + j] = (uint16_t)hb;
+    hlo[q * RPS + j] = (uint16_t)lb;
+  }
+  __syncthreads();
+
+  // ranks past r in a live group are never used
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      const int kk = ks * 16 + kg * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[u][ks][e] = (kk + e < r) ? bv[u][ks][e] : (short)0;
+    }
+
+  float* sw = stage[w];
+#pragma unroll
+  for (int q = 0; q < MT; ++q) {
+    s16x4 hb[RT], lb[RT];
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      if (ks >= ntr) break;
+      hb[ks] = *(const s16x4*)(hhi + (q * 16 + m) * RPS + ks * 16 + kg * 4);
+      lb[ks] = *(const s16x4*)(hlo + (q * 16 + m) * RPS + ks * 16 + kg * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < RT; ++ks) {
+        if (ks >= ntr) break;
+        o = mfma_k16(bv[u][ks], hb[ks], o);
+        o = mfma_k16(bv[u][ks], lb[ks], o);
+      }
+      // o[ii] = delta[token m][column 16u + 4kg + ii]
+      *(f32x4*)(sw + m * SRW + u * 16 + kg * 4) = o;
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = prow + 8 * hh;
+      const f32x4 d0 = *(const f32x4*)(sw + row * SRW + 8 * ppc);
+      const f32x4 d1 = *(const f32x4*)(sw + row * SRW + 8 * ppc + 4);
+      const u32x4 yy = yv[q][hh];
+      const int t = tok[q * 16 + row];
+      bstore16(y_r, (pcol && t >= 0) ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u : kOOB,
+               u32x4{pack_bf16x2(bf16lo(yy.x) + d0.x, bf16hi(yy.x) + d0.y),
+                     pack_bf16x2(bf16lo(yy.y) + d0.z, bf16hi(yy.y) + d0.w),
+                     pack_bf16x2(bf16lo(yy.z) + d1.x, bf16hi(yy.z) + d1.y),
+                     pack_bf16x2(bf16lo(yy.w) + d1.z, bf16hi(yy.w) + d1.w)});
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+namespace {
+
+int rt_of(int R) {
+  const int RT = (R + 15) / 16;
+  return RT <= 1 ? 1 : RT <= 2 ? 2 : RT <= 4 ? 4 : RT <= 8 ? 8 : 16;
+}
+
+}  // namespace
+
+bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in) {
+  if (dtype != kDtypeBF16 || R > 256) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t out = st.off[st.n];
+  if ((int64_t)T * in * 2 >= lim || (int64_t)T * out * 2 >= lim ||
+      (int64_t)out * R * 2 >= lim || (int64_t)R * in * 2 >= lim)
+    return false;
+  for (int i = 0; i < st.n; ++i)
+    if ((st.off[i + 1] - st.off[i]) % 16 != 0) return false;
+  return true;
+}
+
+int sgmv_kparts(int in) {
+  const int kp = in / 1024;
+  return kp < 1 ? 1 : kp > 8 ? 8 : kp;
+}
+
+hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
+                              int R, const int32_t* order, const int32_t* indptr,
+                              const int32_t* ranks, float* h, float* parts, int kparts,
+                              hipStream_t stream) {
+  if (T <= kLong) return hipSuccess;   // no segment can be long
+  if (kparts < 1 || (kparts > 1 && !parts)) return hipErrorInvalidValue;
+  const int64_t stride = (int64_t)T * S * R;
+  const int64_t items = (int64_t)S * kparts * ((T + kBMs - 1) / kBMs + slots);
+  const int64_t grid = 8 * ((items + 7) / 8);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  float* dst = kparts > 1 ? parts : h;
+#define L(RTV)                                                                                 \
+  hipLaunchKernelGGL(k_sgmv_shrink<RTV>, dim3((unsigned)grid), dim3(512), 0, stream, x, T, in, \
+                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride)
+  switch (rt_of(R)) {
+    case 1: L(1); break;
+    case 2: L(2); break;
+    case 4: L(4); break;
+    case 8: L(8); break;
+    default: L(16); break;
+  }
+#undef L
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || kparts == 1) return e;
+  const int64_t n = (int64_t)T * (S * R / 4);
+  hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, parts,
+                     kparts, stride, h, T, S * R, slots, R, order, indptr, ranks);
+  return hipGetLastError();
+}
+
+hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float* h, const void* b,
+                              int slots, int R, const int32_t* order, const int32_t* indptr,
+                              const int32_t* ranks, const float* scalings, hipStream_t stream) {
+  if (T <= kLong) return hipSuccess;
+  int nck = 0;
+  for (int i = 0; i < st.n; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
+  const int64_t items = (int64_t)nck * ((T + kBMe - 1) / kBMe + slots);
+  const int64_t grid = 8 * ((items + 7) / 8);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+#define L(RTV)                                                                                 \
+  hipLaunchKernelGGL(k_sgmv_expand<RTV>, dim3((unsigned)grid), dim3(256), 0, stream, y, T, st, \
+                     h, b, slots, R, order, indptr, ranks, scalings)
+  switch (rt_of(R)) {
+    case 1: L(1); break;
+    case 2: L(2); break;
+    case 4: L(4); break;
+    case 8: L(8); break;
+    default: L(16); break;
+  }
+#undef L
+  return hipGetLastError();
+}
+
+}  // namespace lora

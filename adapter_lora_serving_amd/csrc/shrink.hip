@@ -17,7 +17,8 @@
 // are deterministic run to run.
 //
 // Extra workgroups after the compute items write the zeros: one thread per
-// (position, column) with column % R >= rank(slot).
+// (position, column) with column % R >= rank(slot). Segments longer than
+// max_seg are left to the SGMV kernel (their zeros are still written here).
 #include "lora_common.h"
 #include "lora_kernels.h"
 
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(256) void k_shrink_valu(const void* __restrict__ x_
                                                      int R, const int32_t* __restrict__ token_order,
                                                      const int32_t* __restrict__ indptr,
                                                      const int32_t* __restrict__ ranks,
-                                                     float* __restrict__ h, int n_compute) {
+                                                     float* __restrict__ h, int n_compute,
+                                                     int max_seg) {
   __shared__ int scratch[24];
   __shared__ float part[4][64];
   const int SR = S * R;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void k_shrink_valu(const void* __restrict__ x_
     int b0, n;
     segment_of(indptr, s, T, b0, n);
     const int r = clamp_rank(ranks[s], R);
-    return (n > 0 && r > 0) ? S * ((r + kRG - 1) / kRG) * ((n + kTG - 1) / kTG) : 0;
+    return (n > 0 && n <= max_seg && r > 0) ? S * ((r + kRG - 1) / kRG) * ((n + kTG - 1) / kTG) : 0;
   };
   const SlotItem it = locate_item(blockIdx.x, slots, count, scratch);
   if (it.slot < 0) return;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(256) void k_shrink_valu(const void* __restrict__ x_
 
 hipError_t launch_shrink(int dtype, const void* x, int T, int in, const void* a, int slots,
                          int S, int R, const int32_t* token_order, const int32_t* indptr,
-                         const int32_t* ranks, float* h, hipStream_t stream) {
+                         const int32_t* ranks, float* h, int max_seg, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // upper bound of compute items: sum over slots of S*ceil(r/8)*ceil(n/8)
   const int64_t n_compute = (int64_t)S * ((R + kRG - 1) / kRG) * ((T + kTG - 1) / kTG + slots);
@@ -168,10 +170,10 @@ hipError_t launch_shrink(int dtype, const void* x, int T, int in, const void* a,
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (dtype == kDtypeBF16)
     hipLaunchKernelGGL(k_shrink_valu<BF16>, dim3((unsigned)grid), dim3(256), 0, stream, x, T, in,
-                       a, slots, S, R, token_order, indptr, ranks, h, (int)n_compute);
+                       a, slots, S, R, token_order, indptr, ranks, h, (int)n_compute, max_seg);
   else
     hipLaunchKernelGGL(k_shrink_valu<F32>, dim3((unsigned)grid), dim3(256), 0, stream, x, T, in, a,
-                       slots, S, R, token_order, indptr, ranks, h, (int)n_compute);
+                       slots, S, R, token_order, indptr, ranks, h, (int)n_compute, max_seg);
   return hipGetLastError();
 }
 
