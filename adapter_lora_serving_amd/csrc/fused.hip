@@ -34,7 +34,6 @@ namespace lora {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMT = 16;               // tokens per block (MFMA M / N tile)
 
@@ -43,12 +42,6 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) {
 }
 __device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
 
-__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 // LDS layout of one workgroup of NW waves (bytes):
 //   [0, 64)        tok[16]     token index per block row, -1 for padding
@@ -144,8 +137,10 @@ __device__ __forceinline__ void shrink_slice(const char* __restrict__ x, int in,
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt)
-        if (nt * 16 < r) acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
+      for (int nt = 0; nt < RT; ++nt) {
+        if (nt * 16 >= r) break;   // r is uniform: a scalar branch, no select
+        acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
+      }
   }
   // lane (m, kg) holds D[4kg + ii][m] = h[token 4kg+ii][row nt*16 + m]
   float* mine = red + w * kMT * RP;
@@ -195,11 +190,10 @@ __device__ __forceinline__ void expand_range(char* __restrict__ y, int out, cons
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < RT; ++ks) {
-        if (ks * 16 < r) {
-          const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
-          acc = mfma_k16(b4, hb[ks], acc);
-          acc = mfma_k16(b4, lb[ks], acc);
-        }
+        if (ks * 16 >= r) break;
+        const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
+        acc = mfma_k16(b4, hb[ks], acc);
+        acc = mfma_k16(b4, lb[ks], acc);
       }
       if (t >= 0) {
         const int c = lo + (tile0 + u) * 16;
@@ -283,8 +277,10 @@ __device__ __forceinline__ void shrink_steps(rsrc_t x_r, rsrc_t a_r, uint32_t ro
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt)
-        if (nt * 16 < r) acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
+      for (int nt = 0; nt < RT; ++nt) {
+        if (nt * 16 >= r) break;   // r is uniform: a scalar branch, no select
+        acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
+      }
   }
 }
 
@@ -422,11 +418,10 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < RT; ++ks) {
-      if (ks * 16 < r) {
-        const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
-        o = mfma_k16(b4, hb[ks], o);
-        o = mfma_k16(b4, lb[ks], o);
-      }
+      if (ks * 16 >= r) break;
+      const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
+      o = mfma_k16(b4, hb[ks], o);
+      o = mfma_k16(b4, lb[ks], o);
     }
     const uint32_t off = (live && tile < ntiles)
                              ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
@@ -442,13 +437,12 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < RT; ++ks) {
-      if (ks * 16 < r) {
-        const int kk = ks * 16 + kg * 4;
-        const uint32_t boff = kk < r ? ((uint32_t)(c + m) * (uint32_t)R + kk) * 2u : kOOB;
-        const s16x4 b4 = mask_b4(__builtin_bit_cast(s16x4, bload8(b_r, boff)), kk, r);
-        o = mfma_k16(b4, hb[ks], o);
-        o = mfma_k16(b4, lb[ks], o);
-      }
+      if (ks * 16 >= r) break;
+      const int kk = ks * 16 + kg * 4;
+      const uint32_t boff = kk < r ? ((uint32_t)(c + m) * (uint32_t)R + kk) * 2u : kOOB;
+      const s16x4 b4 = mask_b4(__builtin_bit_cast(s16x4, bload8(b_r, boff)), kk, r);
+      o = mfma_k16(b4, hb[ks], o);
+      o = mfma_k16(b4, lb[ks], o);
     }
     const uint32_t off = live ? yrow + (uint32_t)(c + 4 * kg) * 2u : kOOB;
     const u32x2 yy = bload8(d.y_r, off);
@@ -479,7 +473,7 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = tid / kWave;
+  const int w = wave_id();
   const int S = st.n;
   const int SR = S * R;
   const int out = st.off[S];

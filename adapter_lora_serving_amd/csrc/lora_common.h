@@ -14,6 +14,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Element tags: BF16 data is handled as raw 16-bit patterns packed two per
 // 32-bit word; F32 data as floats. Both move in 16-byte vectors.
@@ -45,6 +46,36 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// D[16x16] += A[16 x 16] . B[16 x 16]^T in fp32 (v_mfma_f32_16x16x16_bf16):
+// lane (m = lane & 15, g = lane >> 4) supplies row m, k in [4g, 4g+4) of
+// both operands; it receives D[4g + i][m] in element i.
+__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// D[16x16] += A[16 x 32] . B[16 x 32]^T in fp32, where lane (m, g) supplies
+// row m, k in [8g, 8g+8) of both operands (the 16x16x32 operand layout).
+// Issued as two 16x16x16 products over the two halves of each lane's eight
+// k values: A and B are split alike, so every k meets its partner once. The
+// single v_mfma_f32_16x16x32_bf16 is not used because the compiler spaces a
+// vector read of its result as for a 4-pass op, and such a read was measured
+// to return the last accumulator register stale on gfx950.
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  const u32x4 au = __builtin_bit_cast(u32x4, a);
+  const u32x4 bu = __builtin_bit_cast(u32x4, b);
+  c = mfma_k16(__builtin_bit_cast(s16x4, u32x2{au.x, au.y}),
+               __builtin_bit_cast(s16x4, u32x2{bu.x, bu.y}), c);
+  return mfma_k16(__builtin_bit_cast(s16x4, u32x2{au.z, au.w}),
+                  __builtin_bit_cast(s16x4, u32x2{bu.z, bu.w}), c);
+}
+
+// Index of the calling wave in its workgroup, in a scalar register: every
+// lane of a wave has the same value, and saying so lets the compiler keep
+// per-wave loops as scalar loops instead of masked vector ones.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64u));
+}
 
 __device__ __forceinline__ int clamp_rank(int r, int R) { return r < 0 ? 0 : (r > R ? R : r); }
 

@@ -30,7 +30,6 @@ namespace lora {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLong = 16;     // segments longer than this take the SGMV path
 constexpr int kBMe = 64;      // tokens per expand item
@@ -38,12 +37,6 @@ constexpr int kCC = 256;      // output columns per expand item
 constexpr int kKC = 64;       // K elements per staged chunk
 constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
 
-__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 // XCD-contiguous item index of block b among n items; -1 past the end.
 __device__ __forceinline__ int xcd_item(int b, int n) {
@@ -86,7 +79,7 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = tid / kWave;
+  const int w = wave_id();
   auto count = [&](int s) -> int {
     int b0, n;
     segment_of(indptr, s, T, b0, n);
@@ -261,7 +254,7 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = tid / kWave;
+  const int w = wave_id();
   const int S = st.n;
   const int out = st.off[S];
   // column chunks: slice i holds ceil(w_i / kCC) chunks

@@ -37,7 +37,8 @@ import workloads as W  # noqa: E402
 from adapter_lora_serving_amd.roofline import HBM_PEAK_GBS, workload_cost  # noqa: E402
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["lora_common.h", "lora_kernels.h", "fused.hip", "shrink.hip", "expand.hip"]
+KERNEL_SOURCES = ["lora_common.h", "lora_kernels.h", "fused.hip", "sgmv.hip", "shrink.hip", "expand.hip",
+                  "lora_api.cpp"]
 
 
 def eprint(*a):
