@@ -104,52 +104,6 @@ __device__ __forceinline__ void update_y4(char* __restrict__ y, int64_t off, u32
   *(u32x2*)(y + off) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
 }
 
-// h[q][j] (partial over this wave's K steps) for the 16 block tokens and the
-// RT*16 rows of one slice; written to red[w].
-template <int RT, int NW>
-__device__ __forceinline__ void shrink_slice(const char* __restrict__ x, int in,
-                                             const int* tok, const char* __restrict__ arow,
-                                             int r, float* red, int lane, int w) {
-  constexpr int RP = RT * 16;
-  constexpr int U = RT <= 1 ? 8 : RT <= 2 ? 4 : RT <= 4 ? 2 : 1;   // K steps in flight per wave
-  const int m = lane & 15;
-  const int kg = lane >> 4;
-  const int t = tok[m];
-  const char* xr = x + (int64_t)(t < 0 ? 0 : t) * in * 2;
-  f32x4 acc[RT];
-#pragma unroll
-  for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nsteps = (in + 31) / 32;
-  for (int st0 = w * U; st0 < nsteps; st0 += NW * U) {
-    bf16x8 xa[U];
-    bf16x8 av[U][RT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (st0 + u) * 32 + kg * 8;
-      const bool kv = (st0 + u) < nsteps && k < in;
-      xa[u] = (kv && t >= 0) ? ld_bf16x8(xr + (int64_t)k * 2) : zero_bf16x8();
-#pragma unroll
-      for (int nt = 0; nt < RT; ++nt) {
-        const int j = nt * 16 + m;
-        av[u][nt] = (kv && j < r) ? ld_bf16x8(arow + ((int64_t)j * in + k) * 2) : zero_bf16x8();
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int nt = 0; nt < RT; ++nt) {
-        if (nt * 16 >= r) break;   // r is uniform: a scalar branch, no select
-        acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
-      }
-  }
-  // lane (m, kg) holds D[4kg + ii][m] = h[token 4kg+ii][row nt*16 + m]
-  float* mine = red + w * kMT * RP;
-#pragma unroll
-  for (int nt = 0; nt < RT; ++nt)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) mine[(4 * kg + ii) * RP + nt * 16 + m] = acc[nt][ii];
-}
-
 // y[tok][c] += sum_j B[c][j] * (hhi + hlo)[tok][j] for columns [lo, hi) of the
 // current slice (lo, hi multiples of 16).
 template <int RT, int NW>
@@ -254,34 +208,61 @@ __device__ __forceinline__ int lane_token(const int32_t* __restrict__ tokp, int 
   return t;
 }
 
-// acc[nt] += x_block . A_rows^T over K steps [s0, s1) (32 elements each);
-// this wave takes steps s0 + w*U + (NW*U)*j + u.
-template <int RT, int NW>
-__device__ __forceinline__ void shrink_steps(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int r,
-                                             uint32_t xrow, bool live, int s0, int s1,
-                                             f32x4 (&acc)[RT], int m, int kg, int w) {
-  constexpr int U = RT <= 1 ? 8 : RT <= 2 ? 4 : RT <= 4 ? 2 : 1;
+// acc[nt] += x_block . A_rows(nt)^T for the first NT rank tiles, over K
+// steps [s0, s1) of 32 elements; this wave takes steps s0 + w*U + (NW*U)*j + u.
+// All U*(NT+1) loads of an iteration are issued before its products, and
+// none is conditional: rows at or past the rank, padding tokens and k past
+// `in` read as zeros through the buffer range check (kOOB).
+template <int NT, int NW>
+__device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
+                                               uint32_t xrow, int s0, int s1, f32x4* acc,
+                                               int m, int kg, int w) {
+  constexpr int U = NT <= 1 ? 8 : NT <= 2 ? 4 : NT <= 4 ? 2 : 1;   // K steps in flight
   for (int st0 = s0 + w * U; st0 < s1; st0 += NW * U) {
-    bf16x8 av[U][RT];
+    bf16x8 av[U][NT];
     bf16x8 xa[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t kb = (uint32_t)((st0 + u) * 32 + kg * 8) * 2u;
-      const bool kv = (st0 + u) < s1;
+      const int k = (st0 + u) * 32 + kg * 8;
+      const bool kv = (st0 + u) < s1 && k < in;
+      const uint32_t kb = (uint32_t)k * 2u;
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
         av[u][nt] = __builtin_bit_cast(
             bf16x8, bload16(a_r, kv ? (uint32_t)(nt * 16 + m) * rowA + kb : kOOB));
-      xa[u] = __builtin_bit_cast(bf16x8, bload16(x_r, (live && kv) ? xrow + kb : kOOB));
+      xa[u] = __builtin_bit_cast(bf16x8, bload16(x_r, (kv && xrow != kOOB) ? xrow + kb : kOOB));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int nt = 0; nt < RT; ++nt) {
-        if (nt * 16 >= r) break;   // r is uniform: a scalar branch, no select
-        acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
-      }
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
   }
+}
+
+// acc[nt] += x_block . A_rows(nt)^T over K steps [s0, s1) for the rank tiles
+// that hold rows below r, rounded up to a power of two (so at most twice the
+// products are formed, and tiles past r add zeros). One loop per tile count:
+// the tile count is uniform, so the choice is a scalar branch taken once, and
+// the loop bodies hold no per-tile conditions. xrow is the byte offset of the
+// lane's x row, or kOOB for a padding token.
+template <int RT, int NW>
+__device__ __forceinline__ void shrink_steps(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
+                                             int r, uint32_t xrow, int s0, int s1,
+                                             f32x4 (&acc)[RT], int m, int kg, int w) {
+  const int ntr = (r + 15) >> 4;
+  if constexpr (RT >= 16) {
+    if (ntr > 8) return shrink_steps_n<16, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
+  }
+  if constexpr (RT >= 8) {
+    if (ntr > 4) return shrink_steps_n<8, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
+  }
+  if constexpr (RT >= 4) {
+    if (ntr > 2) return shrink_steps_n<4, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
+  }
+  if constexpr (RT >= 2) {
+    if (ntr > 1) return shrink_steps_n<2, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
+  }
+  shrink_steps_n<1, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
 }
 
 template <int RT>
@@ -311,7 +292,7 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
   f32x4 acc[RT];
 #pragma unroll
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  shrink_steps<RT, NW>(d.x_r, a_r, rowA, r, live ? (uint32_t)t * rowA : kOOB, live, s0, s1, acc,
+  shrink_steps<RT, NW>(d.x_r, a_r, rowA, d.in, r, live ? (uint32_t)t * rowA : kOOB, s0, s1, acc,
                        m, kg, w);
   store_partial<RT>(red + w * kMT * RP, acc, m, kg);
   __syncthreads();
@@ -398,7 +379,7 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     f32x4 acc[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    shrink_steps<RT, NW>(d.x_r, a_r, rowA, r, live ? (uint32_t)t * rowA : kOOB, live, 0,
+    shrink_steps<RT, NW>(d.x_r, a_r, rowA, d.in, r, live ? (uint32_t)t * rowA : kOOB, 0,
                          (d.in + 31) / 32, acc, m, kg, w);
     store_partial<RT>(red + w * kMT * RP, acc, m, kg);
     __syncthreads();
@@ -543,8 +524,19 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   const float scale = scalings[s];
   const char* ab = (const char*)a_ + (int64_t)s * SR * in * 2;
   const char* bb = (const char*)b_ + (int64_t)s * out * R * 2;
+  const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
+  const uint32_t rowA = (uint32_t)in * 2u;
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const int t = tok[m];
+  const uint32_t xrow = t >= 0 ? (uint32_t)t * rowA : kOOB;
   for (int i = 0; i < S; ++i) {
-    shrink_slice<RT, NW>((const char*)x_, in, tok, ab + (int64_t)i * R * in * 2, r, red, lane, w);
+    const rsrc_t a_r = make_rsrc(ab + (int64_t)i * R * in * 2, (uint32_t)r * rowA);
+    f32x4 acc[RT];
+#pragma unroll
+    for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    shrink_steps<RT, NW>(x_r, a_r, rowA, in, r, xrow, 0, (in + 31) / 32, acc, m, kg, w);
+    store_partial<RT>(red + w * kMT * RT * 16, acc, m, kg);
     __syncthreads();
     reduce_split<RT, NW>(red, scale, hhi, hlo, tid);
     __syncthreads();

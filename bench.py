@@ -2,18 +2,21 @@
 """Throughput of the batched multi-LoRA delta on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the device-side
-addressing build, then the fused shrink + expand (lora_apply_linear) of the
-target. The default workload is the decode BGMV batch: T=256 tokens, one per
-request, in=4096, fused q/k/v out_slices (4096, 1024, 1024), 32 adapter slots
-with ranks in {8, 16} (R=16), scaling 2, bf16, seeded synthetic data.
+addressing build, then the fused shrink + expand (lora_apply_linear) of a
+linear target, or gather_shrink + expand of an embedding target. The default
+workload is the decode BGMV batch: T=256 tokens, one per request, in=4096,
+fused q/k/v out_slices (4096, 1024, 1024), 32 adapter slots with ranks in
+{8, 16} (R=16), scaling 2, bf16, seeded synthetic data. `--config 3|4|5`
+times the prefill, embedding and skewed-mix batches the same way.
 
 Timing: the inputs of `--sets` independent buffer sets are resident in HBM
 (more than 1 GiB in total, so the 256 MB Infinity Cache cannot serve them);
 step i uses set i mod sets. The K timed steps are recorded once in a hipGraph
 (through torch.cuda.CUDAGraph) and replayed once between two synchronisations,
 so host launch overhead is not measured. The dominant kernel's average launch
-duration comes from HIP events around a second graph that launches only
-lora_apply_linear K times on the same stream.
+duration comes from HIP events around a second graph that launches only the
+apply (lora_apply_linear, or gather_shrink + expand) K times on the same
+stream.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -34,7 +37,7 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 import workloads as W  # noqa: E402
-from adapter_lora_serving_amd.roofline import HBM_PEAK_GBS, workload_cost  # noqa: E402
+from adapter_lora_serving_amd.roofline import BF16_MFMA_PEAK_TFLOPS, HBM_PEAK_GBS, workload_cost  # noqa: E402
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["lora_common.h", "lora_kernels.h", "fused.hip", "sgmv.hip", "shrink.hip", "expand.hip",
@@ -123,12 +126,10 @@ def main():
 
     wl = W.make_config(args.config, seed=0)
     tg = wl.target(args.target)
-    if tg.embedding:
-        eprint("bench.py times linear targets (apply_linear); use the tests for config 4")
-        sys.exit(1)
     alg_bytes, alg_flops, terms = workload_cost(wl, tg)
     eb = 2 if wl.dtype == "bf16" else 4
-    set_bytes = (tg.x.size + tg.a.size + tg.b.size + tg.y0.size) * eb
+    x_bytes = tg.ids.size * 4 if tg.embedding else tg.x.size * eb
+    set_bytes = x_bytes + (tg.a.size + tg.b.size + tg.y0.size) * eb
     n_sets = args.sets or int(min(64, max(2, math.ceil(1.1 * 2 ** 30 / set_bytes))))
     eprint(f"workload {wl.name}/{tg.name}: T={wl.T} in={tg.in_features} out={tg.out_slices} "
            f"R={wl.R} slots={wl.slots}; algorithmic {alg_bytes / 1e6:.2f} MB/call "
@@ -143,25 +144,35 @@ def main():
     scal = torch.from_numpy(wl.scalings).to(dev)
     ts_host = torch.from_numpy(wl.token_slot.astype(np.int32))
     sets = []
-    x0, a0, b0, y0 = d(tg.x), d(tg.a), d(tg.b), d(tg.y0)
+    if tg.embedding:
+        x0 = torch.from_numpy(tg.ids.astype(np.int32)).to(dev)
+    else:
+        x0 = d(tg.x)
+    a0, b0, y0 = d(tg.a), d(tg.b), d(tg.y0)
     for i in range(n_sets):
         s = dict(x=x0.clone(), a=a0.clone(), b=b0.clone(), y=y0.clone(), ts=ts_host.to(dev))
         s["addr"] = L.build_addressing(s["ts"], wl.slots)
         sets.append(s)
     del x0, a0, b0, y0
-    need = L.workspace_bytes(wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    if tg.embedding:
+        h = torch.empty(wl.T, wl.R, dtype=torch.float32, device=dev)
+    else:
+        need = L.workspace_bytes(wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def apply_only(i):
+        s = sets[i % n_sets]
+        if tg.embedding:
+            L.gather_shrink(s["x"], s["a"], s["addr"], ranks, out=h)
+            L.expand_(h, s["b"], s["addr"], ranks, scal, s["y"], tg.out_slices)
+        else:
+            L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal,
+                            tg.out_slices, workspace=ws)
 
     def step(i):
         s = sets[i % n_sets]
         L.build_addressing(s["ts"], wl.slots, out=s["addr"])
-        L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal, tg.out_slices,
-                        workspace=ws)
-
-    def apply_only(i):
-        s = sets[i % n_sets]
-        L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal, tg.out_slices,
-                        workspace=ws)
+        apply_only(i)
 
     def addr_only(i):
         s = sets[i % n_sets]
@@ -220,12 +231,12 @@ def main():
 
     achieved = alg_bytes / (ms_apply * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_step * 1e-3)
-    eprint(f"step {ms_step * 1e3:.2f} us (addressing {ms_addr * 1e3:.2f} us, apply_linear "
+    eprint(f"step {ms_step * 1e3:.2f} us (addressing {ms_addr * 1e3:.2f} us, apply "
            f"{ms_apply * 1e3:.2f} us/launch = {achieved:.0f} GB/s algorithmic); device copy "
            f"{copy_gbs:.0f} GB/s")
 
     result = {
-        "metric": "LoRA-delta tokens/sec (decode BGMV, addressing + fused shrink/expand)",
+        "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill)",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -242,7 +253,7 @@ def main():
                    "slots": wl.slots, "buffer_sets": n_sets},
         "roofline": {
             "bound": "hbm",
-            "kernel": "lora_apply_linear",
+            "kernel": "lora_gather_shrink + lora_expand" if tg.embedding else "lora_apply_linear",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -251,6 +262,7 @@ def main():
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "avg_launch_us": round(ms_apply * 1e3, 3),
         },
+        "mfma_util": round(alg_flops / (ms_apply * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 5),
         "addressing_us": round(ms_addr * 1e3, 3),
         "device_copy_gbs": round(copy_gbs, 1),
     }

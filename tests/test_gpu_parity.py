@@ -232,6 +232,15 @@ EDGE = {
     "wide_S8": dict(T=90, in_f=96, out_slices=(8, 16, 24, 32, 40, 48, 56, 64), R=128, slots=3,
                     ranks=[128, 100, 7]),
     "long_seg": dict(T=3000, in_f=384, out_slices=(512, 256), R=64, slots=3, ranks=[64, 48, 8]),
+    # `in` a multiple of 8 but not of 32: the last K step of every MFMA path is partial
+    "ragged_k_decode": dict(T=200, in_f=520, out_slices=(64, 32, 32), R=16, slots=24,
+                            ranks=[16, 8] * 12, dead=0.05),
+    "ragged_k_mixed": dict(T=700, in_f=1000, out_slices=(128, 64), R=32, slots=40,
+                           ranks=[32, 16, 5, 0] * 10),
+    "ragged_k_long": dict(T=1500, in_f=1000, out_slices=(128, 64), R=32, slots=3,
+                          ranks=[32, 16, 5]),
+    "ragged_k_rank128": dict(T=1100, in_f=776, out_slices=(256, 64, 64), R=128, slots=70,
+                             ranks=[128, 64, 8, 100, 0] * 14),
 }
 
 
