@@ -195,17 +195,13 @@ struct DecodeArgs {
   int spin_limit;
 };
 
-// Token id of lane row m (scalar loads of the block's 16 ids, clamped into
-// the array; each lane then selects its own).
+// Token id of lane row m: one vector load per lane (index clamped into the
+// array). Issued before the bulk A / B loads, it is the oldest load in
+// flight, so the first use of the id waits for it alone (vector loads
+// complete in order), not for the bulk loads issued after it.
 __device__ __forceinline__ int lane_token(const int32_t* __restrict__ tokp, int T, int seg0,
                                           int m) {
-  int toks[kMT];
-#pragma unroll
-  for (int k = 0; k < kMT; ++k) toks[k] = tokp[min(seg0 + k, T - 1)];
-  int t = toks[0];
-#pragma unroll
-  for (int k = 1; k < kMT; ++k) t = (m == k) ? toks[k] : t;
-  return t;
+  return tokp[min(seg0 + m, T - 1)];
 }
 
 // acc[nt] += x_block . A_rows(nt)^T for the first NT rank tiles, over K
@@ -213,29 +209,50 @@ __device__ __forceinline__ int lane_token(const int32_t* __restrict__ tokp, int 
 // All U*(NT+1) loads of an iteration are issued before its products, and
 // none is conditional: rows at or past the rank, padding tokens and k past
 // `in` read as zeros through the buffer range check (kOOB).
-template <int NT, int NW>
+template <int NT, int NW, class XRow>
 __device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
-                                               uint32_t xrow, int s0, int s1, f32x4* acc,
+                                               XRow xrow_of, int s0, int s1, f32x4* acc,
                                                int m, int kg, int w) {
   constexpr int U = NT <= 1 ? 8 : NT <= 2 ? 4 : NT <= 4 ? 2 : 1;   // K steps in flight
-  for (int st0 = s0 + w * U; st0 < s1; st0 += NW * U) {
-    bf16x8 av[U][NT];
-    bf16x8 xa[U];
+  int st0 = s0 + w * U;
+  if (st0 >= s1) return;
+  bf16x8 av[U][NT];
+  bf16x8 xa[U];
+  auto load_a = [&](int st) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (st0 + u) * 32 + kg * 8;
-      const bool kv = (st0 + u) < s1 && k < in;
-      const uint32_t kb = (uint32_t)k * 2u;
+      const int k = (st + u) * 32 + kg * 8;
+      const bool kv = (st + u) < s1 && k < in;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         av[u][nt] = __builtin_bit_cast(
-            bf16x8, bload16(a_r, kv ? (uint32_t)(nt * 16 + m) * rowA + kb : kOOB));
-      xa[u] = __builtin_bit_cast(bf16x8, bload16(x_r, (kv && xrow != kOOB) ? xrow + kb : kOOB));
+            bf16x8, bload16(a_r, kv ? (uint32_t)(nt * 16 + m) * rowA + (uint32_t)k * 2u : kOOB));
     }
+  };
+  auto load_x = [&](int st, uint32_t xrow) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (st + u) * 32 + kg * 8;
+      const bool kv = (st + u) < s1 && k < in && xrow != kOOB;
+      xa[u] = __builtin_bit_cast(bf16x8, bload16(x_r, kv ? xrow + (uint32_t)k * 2u : kOOB));
+    }
+  };
+  auto products = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_k32(xa[u], av[u][nt], acc[nt]);
+  };
+  // first iteration: A is requested before the x row offset is formed, so
+  // the token id's latency overlaps the A loads
+  load_a(st0);
+  const uint32_t xrow = xrow_of();
+  load_x(st0, xrow);
+  products();
+  for (st0 += NW * U; st0 < s1; st0 += NW * U) {
+    load_a(st0);
+    load_x(st0, xrow);
+    products();
   }
 }
 
@@ -243,11 +260,11 @@ __device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t 
 // that hold rows below r, rounded up to a power of two (so at most twice the
 // products are formed, and tiles past r add zeros). One loop per tile count:
 // the tile count is uniform, so the choice is a scalar branch taken once, and
-// the loop bodies hold no per-tile conditions. xrow is the byte offset of the
-// lane's x row, or kOOB for a padding token.
-template <int RT, int NW>
+// the loop bodies hold no per-tile conditions. xrow() gives the byte offset of
+// the lane's x row, or kOOB for a padding token.
+template <int RT, int NW, class XRow>
 __device__ __forceinline__ void shrink_steps(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
-                                             int r, uint32_t xrow, int s0, int s1,
+                                             int r, XRow xrow, int s0, int s1,
                                              f32x4 (&acc)[RT], int m, int kg, int w) {
   const int ntr = (r + 15) >> 4;
   if constexpr (RT >= 16) {
@@ -292,8 +309,9 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
   f32x4 acc[RT];
 #pragma unroll
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  shrink_steps<RT, NW>(d.x_r, a_r, rowA, d.in, r, live ? (uint32_t)t * rowA : kOOB, s0, s1, acc,
-                       m, kg, w);
+  shrink_steps<RT, NW>(
+      d.x_r, a_r, rowA, d.in, r, [&] { return live ? (uint32_t)t * rowA : kOOB; }, s0, s1, acc,
+      m, kg, w);
   store_partial<RT>(red + w * kMT * RP, acc, m, kg);
   __syncthreads();
   for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
@@ -320,14 +338,14 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;   // tiles per wave in flight
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = lane_token(d.tokp, d.T, seg0, m);
+  const int t = lane_token(d.tokp, d.T, seg0, m);   // oldest load in flight
   const bool live = m < n;
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
 
+  // B tiles first (no dependence on the token id), then the y rows
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
-  const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int tile = w + NW * u;
@@ -339,6 +357,11 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
                                : kOOB;
       bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
     }
+  }
+  const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int tile = w + NW * u;
     yv[u] = bload8(d.y_r, (live && tile < ntiles)
                               ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
                               : kOOB);
@@ -379,8 +402,9 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     f32x4 acc[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    shrink_steps<RT, NW>(d.x_r, a_r, rowA, d.in, r, live ? (uint32_t)t * rowA : kOOB, 0,
-                         (d.in + 31) / 32, acc, m, kg, w);
+    shrink_steps<RT, NW>(
+        d.x_r, a_r, rowA, d.in, r, [&] { return live ? (uint32_t)t * rowA : kOOB; }, 0,
+        (d.in + 31) / 32, acc, m, kg, w);
     store_partial<RT>(red + w * kMT * RP, acc, m, kg);
     __syncthreads();
     reduce_split<RT, NW>(red, scale, hhi, hlo, tid);
@@ -535,7 +559,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     f32x4 acc[RT];
 #pragma unroll
     for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    shrink_steps<RT, NW>(x_r, a_r, rowA, in, r, xrow, 0, (in + 31) / 32, acc, m, kg, w);
+    shrink_steps<RT, NW>(x_r, a_r, rowA, in, r, [&] { return xrow; }, 0, (in + 31) / 32, acc, m,
+                         kg, w);
     store_partial<RT>(red + w * kMT * RT * 16, acc, m, kg);
     __syncthreads();
     reduce_split<RT, NW>(red, scale, hhi, hlo, tid);
