@@ -5,20 +5,22 @@
 // slot) followed by expand (y += scaling * h @ B^T per fused slice), with h
 // kept in fp32 and never written to memory.
 //
-// Work items (one 512-thread workgroup each):
-//  * decode items, for segments of at most 16 tokens: (slot, column chunk),
-//    a chunk lying inside one slice. The workgroup computes that slice's
-//    h [16 x r] itself and expands its chunk. A slice split into several
-//    chunks has its h computed once per chunk: the redundant reads of A and x
-//    hit L2 (items of one slot are placed on one XCD), and in exchange no
-//    workgroup ever waits for another, so the kernel needs no atomics, no
-//    workspace and no fences, and is deterministic.
-//  * prefill items, for longer segments: (slot, block of 16 tokens) over all
-//    slices and every output column, so h is computed once per token block.
+// Work (one 512-thread workgroup per piece or item):
+//  * decode pieces, for segments of at most 16 tokens. A shrink piece
+//    (slot, slice, K part) forms the partial product of the slot's tokens
+//    with the slice's A rows over its part of `in` and stores it as a 16 x RP
+//    fp32 tile in the workspace; an expand piece (slot, column chunk of one
+//    slice) prefetches its B tile and y rows, waits for the slice's KP
+//    partial tiles (a counter handoff, described below), adds them in a
+//    fixed order, and expands its chunk. No byte of A or B is read twice.
+//  * prefill items, for longer segments when the whole batch runs here:
+//    (slot, block of 16 tokens) over every slice and output column; h of the
+//    block stays in LDS.
 // Shrink: K is split across the 8 waves; each wave accumulates a 16x16 tile
-//   (tokens x A rows) per 16 rows with v_mfma_f32_16x16x32_bf16, the waves'
-//   partial tiles are added in a fixed order through LDS. Rows of A at or past
-//   the rank and padding tokens are zeros written into registers, never loaded.
+//   (tokens x A rows) per 16 rank rows on bf16 MFMA, and the waves' partial
+//   tiles are added in a fixed order through LDS. Rows of A at or past the
+//   rank, padding tokens and a partial last K step read as zeros through the
+//   buffer range check.
 // Expand: y^T tile [16 columns x 16 tokens] = B_tile [16 x r] . H^T, with H
 //   (already multiplied by the slot's scaling) split into bf16 hi + lo parts,
 //   two v_mfma_f32_16x16x16_bf16 per 16 ranks and fp32 accumulation, so h is
