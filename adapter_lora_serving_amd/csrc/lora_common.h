@@ -179,6 +179,51 @@ __device__ __forceinline__ SlotItem locate_item(int item, int slots, CountFn cou
   return r;
 }
 
+// As locate_item, with the item chosen from the total: item = pick(total)
+// (the same value in every thread; negative for none). One pass over the
+// slots (each count evaluated once when slots <= blockDim.x), so a
+// workgroup learns its item after a single round of loads. The thread that
+// finds the item calls stash(slot, scratch + 20) to leave up to four ints of
+// per-slot data (read them after the call, before scratch is reused).
+template <typename CountFn, typename PickFn, typename StashFn>
+__device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, CountFn count,
+                                                  int* scratch /* >= 24 ints LDS */,
+                                                  StashFn stash) {
+  const int nthreads = blockDim.x;
+  const int chunk = (slots + nthreads - 1) / nthreads;
+  const int s0 = threadIdx.x * chunk;
+  const int s1 = min(slots, s0 + chunk);
+  int local = 0;
+  int first = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c = count(s);
+    if (s == s0) first = c;
+    local += c;
+  }
+  int total = 0;
+  const int excl = block_exclusive_scan(local, scratch, &total);
+  const int item = pick(total);
+  if (threadIdx.x == 0) { scratch[18] = -1; scratch[19] = 0; }
+  __syncthreads();
+  if (item >= 0 && item >= excl && item < excl + local) {
+    int run = excl;
+    for (int s = s0; s < s1; ++s) {
+      const int c = s == s0 ? first : count(s);
+      if (item < run + c) {
+        scratch[18] = s;
+        scratch[19] = item - run;
+        stash(s, scratch + 20);   // per-slot values the caller wants (up to 4 ints)
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  SlotItem r{scratch[18], scratch[19], total};
+  __syncthreads();
+  return r;
+}
+
 // Raw buffer access. A resource covers [base, base + bytes); a load at an
 // offset outside it returns zero without touching memory and a store there is
 // dropped, so predicated accesses need no branches (kOOB is such an offset

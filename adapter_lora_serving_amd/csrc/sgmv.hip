@@ -86,22 +86,26 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
     return (n > kLong && clamp_rank(ranks[s], R) > 0) ? S * kparts * ((n + kBMs - 1) / kBMs)
                                                       : 0;
   };
-  const int total = locate_item(0x7fffffff, slots, count, scratch).total;
-  const int item = xcd_item(blockIdx.x, total);
-  if (item < 0) return;
-  const SlotItem it = locate_item(item, slots, count, scratch);
+  const SlotItem it = locate_picked(
+      [&](int total) { return xcd_item(blockIdx.x, total); }, slots, count, scratch,
+      [&](int ss, int* v) {
+        segment_of(indptr, ss, T, v[0], v[1]);
+        v[2] = clamp_rank(ranks[ss], R);
+      });
+  if (it.slot < 0) return;
   const int s = it.slot;
-  int seg0, n;
-  segment_of(indptr, s, T, seg0, n);
-  const int r = clamp_rank(ranks[s], R);
+  const int seg0 = scratch[20];
+  const int n = scratch[21];
+  const int r = scratch[22];
   const int nmb = (n + kBMs - 1) / kBMs;
   const int mb = it.local % nmb;
   const int rest = it.local / nmb;
   const int kp = rest % kparts;
   const int i = rest / kparts;
   const int ntok = min(kBMs, n - mb * kBMs);
-  if (tid < kBMs) tok[tid] = tid < ntok ? token_at(order, seg0 + mb * kBMs + tid, T) : -1;
-  __syncthreads();
+  // the token ids are the oldest loads in flight; the first A chunks (which
+  // do not depend on them) are issued next, then the ids are waited for
+  const int tv = token_at(order, seg0 + mb * kBMs + min(tid, ntok - 1), T);
 
   const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
   const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S * R + (int64_t)i * R) * in * 2,
@@ -114,14 +118,30 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
 
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = tok[w * 16 + m];
-  const uint32_t xrow = t >= 0 ? (uint32_t)t * rowG : kOOB;
   const int arow = tid >> 3;        // 0..63 (+64 per extra piece)
   const int apc = tid & 7;
 
   u32x4 xr[D][2];
   u32x4 ar[D][AL];
-  auto issue = [&](int slot, int c) {   // loads of chunk c (relative) into ring slot
+  auto issue_a = [&](int slot, int c) {   // A loads of chunk c (relative) into ring slot
+    const bool cv = c < nch;
+    const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
+#pragma unroll
+    for (int q = 0; q < AL; ++q) {
+      const int row = arow + 64 * q;
+      const uint32_t e = (uint32_t)((cbeg + c) * kKC + apc * 8);
+      ar[slot][q] = bload16(a_r, (cv && row < RP && e < (uint32_t)in)
+                                     ? (uint32_t)row * rowG + kb + apc * 16u
+                                     : kOOB);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue_a(d, d);
+  if (tid < kBMs) tok[tid] = tid < ntok ? tv : -1;
+  __syncthreads();
+  const int t = tok[w * 16 + m];
+  const uint32_t xrow = t >= 0 ? (uint32_t)t * rowG : kOOB;
+  auto issue_x = [&](int slot, int c) {   // x loads of chunk c (relative) into ring slot
     const bool cv = c < nch;
     const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
 #pragma unroll
@@ -130,14 +150,6 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
       xr[slot][ks] = bload16(x_r, (cv && xrow != kOOB && e < (uint32_t)in)
                                       ? xrow + kb + (uint32_t)(ks * 32 + kg * 8) * 2u
                                       : kOOB);
-    }
-#pragma unroll
-    for (int q = 0; q < AL; ++q) {
-      const int row = arow + 64 * q;
-      const uint32_t e = (uint32_t)((cbeg + c) * kKC + apc * 8);
-      ar[slot][q] = bload16(a_r, (cv && row < RP && e < (uint32_t)in)
-                                     ? (uint32_t)row * rowG + kb + apc * 16u
-                                     : kOOB);
     }
   };
   auto stage = [&](int slot, int buf) {   // A chunk in ring slot -> LDS buffer
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
 #pragma unroll
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, d);
+  for (int d = 0; d < D; ++d) issue_x(d, d);
   stage(0, 0);
   __syncthreads();
 #pragma unroll 1
@@ -175,7 +187,8 @@ __global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_
             acc[nt] = mfma_k32(xa, av, acc[nt]);
           }
         }
-        issue(d, c + D);
+        issue_a(d, c + D);
+        issue_x(d, c + D);
         __syncthreads();
       }
     }
@@ -265,14 +278,17 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
     segment_of(indptr, s, T, b0, n);
     return (n > kLong && clamp_rank(ranks[s], R) > 0) ? nck * ((n + kBMe - 1) / kBMe) : 0;
   };
-  const int total = locate_item(0x7fffffff, slots, count, scratch).total;
-  const int item = xcd_item(blockIdx.x, total);
-  if (item < 0) return;
-  const SlotItem it = locate_item(item, slots, count, scratch);
+  const SlotItem it = locate_picked(
+      [&](int total) { return xcd_item(blockIdx.x, total); }, slots, count, scratch,
+      [&](int ss, int* v) {
+        segment_of(indptr, ss, T, v[0], v[1]);
+        v[2] = clamp_rank(ranks[ss], R);
+      });
+  if (it.slot < 0) return;
   const int s = it.slot;
-  int seg0, n;
-  segment_of(indptr, s, T, seg0, n);
-  const int r = clamp_rank(ranks[s], R);
+  const int seg0 = scratch[20];
+  const int n = scratch[21];
+  const int r = scratch[22];
   const int nmb = (n + kBMe - 1) / kBMe;
   const int mb = it.local % nmb;
   int ck = it.local / nmb;
@@ -285,8 +301,9 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   const int lo = st.off[i] + ck * kCC;
   const int hi = min(lo + kCC, st.off[i + 1]);
   const int ntok = min(kBMe, n - mb * kBMe);
-  if (tid < kBMe) tok[tid] = tid < ntok ? token_at(order, seg0 + mb * kBMe + tid, T) : -1;
-  __syncthreads();
+  // the token ids are the oldest loads in flight; the B tiles (which do not
+  // depend on them) are issued next, then the ids are waited for
+  const int tv = token_at(order, seg0 + mb * kBMe + min(tid, ntok - 1), T);
 
   const int m = lane & 15;
   const int kg = lane >> 4;
@@ -296,6 +313,21 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   const int ntiles = (hi - lo) >> 4;
   const int cw = lo + w * 64;         // this wave's first column
   const int ntr = (r + 15) / 16;      // rank tiles holding ranks below r
+  s16x4 bv[TPW][RT];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = w * TPW + u;
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      const int kk = ks * 16 + kg * 4;
+      bv[u][ks] = __builtin_bit_cast(
+          s16x4, bload8(b_r, (tile < ntiles && kk < r)
+                                 ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
+                                 : kOOB));
+    }
+  }
+  if (tid < kBMe) tok[tid] = tid < ntok ? tv : -1;
+  __syncthreads();
 
   // row-major y access: lane -> rows (lane >> 3) and 8 + (lane >> 3) of a
   // token tile, 16-byte piece (lane & 7) of the wave's 128-byte column span
@@ -312,19 +344,6 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
                                    ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
                                    : kOOB);
     }
-  s16x4 bv[TPW][RT];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = w * TPW + u;
-#pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      const int kk = ks * 16 + kg * 4;
-      bv[u][ks] = __builtin_bit_cast(
-          s16x4, bload8(b_r, (tile < ntiles && kk < r)
-                                 ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
-                                 : kOOB));
-    }
-  }
 
   // h rows of the block (only ranks below r are read), scaled, split hi + lo;
   // all of a thread's loads are issued before any is used
