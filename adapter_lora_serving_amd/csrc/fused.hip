@@ -459,6 +459,139 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   }
 }
 
+// ---------------------------------------------------------------------------
+// standalone decode kernels (lora_shrink / lora_expand on segments of at most
+// 16 tokens): the same tiles as the decode pieces, with h in memory
+// ---------------------------------------------------------------------------
+
+// h rows of one (slot, slice) for the slot's <= 16 tokens: K split across the
+// NW waves, partial tiles added in a fixed order; columns below r written
+// (the columns at or past r, and the rows of other tokens, are left to the
+// zero-writing kernel).
+template <int RT, int NW>
+__device__ __forceinline__ void shrink_rows(rsrc_t x_r, rsrc_t a_r, const int32_t* tokp, int T,
+                                            int in, int seg0, int n, int r, float* h, int SR,
+                                            int col0, float* red, int* tok, int lane, int w,
+                                            int tid) {
+  constexpr int RP = RT * 16;
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const int t = lane_token(tokp, T, seg0, m);
+  const bool live = m < n;
+  const uint32_t rowA = (uint32_t)in * 2u;
+  f32x4 acc[RT];
+#pragma unroll
+  for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  shrink_steps<RT, NW>(x_r, a_r, rowA, in, r, [&] { return live ? (uint32_t)t * rowA : kOOB; },
+                       0, (in + 31) / 32, acc, m, kg, w);
+  store_partial<RT>(red + w * kMT * RP, acc, m, kg);
+  if (w == 0 && kg == 0) tok[m] = live ? t : -1;
+  __syncthreads();
+  for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
+    const int q = idx / RP;
+    const int j = idx - q * RP;
+    const int tq = tok[q];
+    if (tq < 0 || j >= r) continue;
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += red[ww * kMT * RP + idx];
+    h[(int64_t)tq * SR + col0 + j] = v;
+  }
+}
+
+// expand of column chunk [lo, hi) of slice i for the slot's <= 16 tokens,
+// with the slice's h rows read from memory
+template <int RT, int NW>
+__device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, const float* h,
+                                            int SR, int col0, int r, float scale, int seg0,
+                                            int n, int lo, int hi, uint16_t* hhi, uint16_t* hlo,
+                                            int* tok, int lane, int w, int tid) {
+  constexpr int RP = RT * 16;
+  constexpr int RPS = RP + 4;
+  constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;   // tiles per wave in flight
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const int t = lane_token(d.tokp, d.T, seg0, m);   // oldest load in flight
+  const bool live = m < n;
+  const int ntiles = (hi - lo) >> 4;
+  const int R = d.R;
+  const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
+
+  s16x4 bv[PT][RT];
+  u32x2 yv[PT];
+  auto load_group = [&](int g) {
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int tile = w + NW * (g * PT + u);
+#pragma unroll
+      for (int ks = 0; ks < RT; ++ks) {
+        const int kk = ks * 16 + kg * 4;
+        const uint32_t off = (tile < ntiles && kk < r)
+                                 ? ((uint32_t)(lo + tile * 16 + m) * (uint32_t)R + kk) * 2u
+                                 : kOOB;
+        bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int tile = w + NW * (g * PT + u);
+      yv[u] = bload8(d.y_r, (live && tile < ntiles)
+                                ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
+                                : kOOB);
+    }
+  };
+  load_group(0);
+  if (w == 0 && kg == 0) tok[m] = live ? t : -1;
+  __syncthreads();
+  // h rows: scaled, split into bf16 hi + lo (ranks at or past r read as 0)
+  const rsrc_t h_r = make_rsrc(h, (uint32_t)d.T * (uint32_t)SR * 4u);
+  for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
+    const int q = idx / RP;
+    const int j = idx - q * RP;
+    const int tq = tok[q];
+    const float v =
+        __uint_as_float(bload4(h_r, (tq >= 0 && j < r)
+                                        ? ((uint32_t)tq * (uint32_t)SR + col0 + j) * 4u
+                                        : kOOB)) *
+        scale;
+    const uint32_t hb = to_bf16_bits(v);
+    const uint32_t lb = to_bf16_bits(v - __uint_as_float(hb << 16));
+    hhi[q * RPS + j] = (uint16_t)hb;
+    hlo[q * RPS + j] = (uint16_t)lb;
+  }
+  __syncthreads();
+
+  s16x4 hb[RT], lb[RT];
+#pragma unroll
+  for (int ks = 0; ks < RT; ++ks) {
+    hb[ks] = *(const s16x4*)(hhi + m * RPS + ks * 16 + kg * 4);
+    lb[ks] = *(const s16x4*)(hlo + m * RPS + ks * 16 + kg * 4);
+  }
+  const int ngroups = (ntiles + NW * PT - 1) / (NW * PT);
+  for (int g = 0; g < ngroups; ++g) {
+    if (g > 0) load_group(g);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int tile = w + NW * (g * PT + u);
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < RT; ++ks) {
+        if (ks * 16 >= r) break;
+        const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
+        o = mfma_k16(b4, hb[ks], o);
+        o = mfma_k16(b4, lb[ks], o);
+      }
+      const uint32_t off = (live && tile < ntiles)
+                               ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
+                               : kOOB;
+      const u32x2 yy = yv[u];
+      bstore8(d.y_r, off,
+              u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
+                    pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
+    }
+  }
+}
+
 }  // namespace
 
 template <int RT, int NW>
@@ -573,6 +706,80 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   }
 }
 
+template <int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_shrink(
+    const void* __restrict__ x_, int T, int in, const void* __restrict__ a_, int slots, int S,
+    int R, const int32_t* __restrict__ token_order, const int32_t* __restrict__ indptr,
+    const int32_t* __restrict__ ranks, float* __restrict__ h) {
+  using L = Lds<RT, NW>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int* tok = (int*)lds;
+  float* red = (float*)(lds + L::kRed);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  // block bid = 8*k + xcd runs on XCD xcd; slot s = 8*q + xcd
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int k = bid >> 3;
+  const int q = k / S;
+  const int i = k - q * S;
+  const int s = q * 8 + xcd;
+  if (s >= slots) return;
+  int seg0, n;
+  segment_of(indptr, s, T, seg0, n);
+  const int r = clamp_rank(ranks[s], R);
+  if (n == 0 || r == 0 || n > kMT) return;
+  const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
+  const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S * R + (int64_t)i * R) * in * 2,
+                               (uint32_t)r * (uint32_t)in * 2u);
+  shrink_rows<RT, NW>(x_r, a_r, token_order, T, in, seg0, n, r, h, S * R, i * R, red, tok, lane,
+                      w, tid);
+}
+
+template <int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_expand(
+    void* __restrict__ y_, int T, SliceTable st, const float* __restrict__ h,
+    const void* __restrict__ b_, int slots, int R, const int32_t* __restrict__ token_order,
+    const int32_t* __restrict__ indptr, const int32_t* __restrict__ ranks,
+    const float* __restrict__ scalings, ChunkTable ct) {
+  using L = Lds<RT, NW>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int* tok = (int*)lds;
+  uint16_t* hhi = (uint16_t*)(lds + L::kHhi);
+  uint16_t* hlo = (uint16_t*)(lds + L::kHlo);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int S = st.n;
+  const int out = st.off[S];
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int k = bid >> 3;
+  const int q = k / ct.n;
+  const int c = k - q * ct.n;
+  const int s = q * 8 + xcd;
+  if (s >= slots) return;
+  int seg0, n;
+  segment_of(indptr, s, T, seg0, n);
+  const int r = clamp_rank(ranks[s], R);
+  if (n == 0 || r == 0 || n > kMT) return;
+  const int i = ct.slice[c];
+  DecodeArgs d;
+  d.y_r = make_rsrc(y_, (uint32_t)T * (uint32_t)out * 2u);
+  d.tokp = token_order;
+  d.T = T;
+  d.in = 0;
+  d.out = out;
+  d.R = R;
+  d.KP = 1;
+  d.spin_limit = 0;
+  const rsrc_t b_r =
+      make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
+  expand_rows<RT, NW>(d, b_r, h, S * R, i * R, r, scalings[s], seg0, n, ct.c0[c], ct.c1[c], hhi,
+                      hlo, tok, lane, w, tid);
+}
+
 namespace {
 
 int rt_bucket(int R) {
@@ -603,6 +810,35 @@ int k_parts(int in) {
   const int env = env_int("LORA_KPARTS", 0);
   int kp = env > 0 ? env : in / 2048;
   return kp < 1 ? 1 : kp > 8 ? 8 : kp;
+}
+
+// Expand chunks: each slice cut into pieces of at most `cols` columns (a
+// multiple of 16), at most kMaxChunks in all.
+ChunkTable make_chunks(const SliceTable& st, int R) {
+  ChunkTable ct;
+  int cols = decode_chunk_cols(R);
+  for (;;) {
+    int n = 0;
+    for (int i = 0; i < st.n; ++i) {
+      const int w = st.off[i + 1] - st.off[i];
+      n += (w + cols - 1) / cols;
+    }
+    if (n <= kMaxChunks) break;
+    cols *= 2;
+  }
+  ct.n = 0;
+  for (int i = 0; i < st.n; ++i) {
+    ct.per_slice[i] = 0;
+    ct.first[i] = ct.n;
+    for (int c = st.off[i]; c < st.off[i + 1]; c += cols) {
+      ct.slice[ct.n] = i;
+      ct.c0[ct.n] = c;
+      ct.c1[ct.n] = min(c + cols, st.off[i + 1]);
+      ++ct.n;
+      ++ct.per_slice[i];
+    }
+  }
+  return ct;
 }
 
 }  // namespace
@@ -641,31 +877,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const int32_t* ranks, const float* scalings, void* workspace,
                               bool with_long, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // expand chunks: each slice cut into pieces of at most `cols` columns
-  // (a multiple of 16), at most kMaxChunks in all
-  ChunkTable ct;
-  int cols = decode_chunk_cols(R);
-  for (;;) {
-    int n = 0;
-    for (int i = 0; i < st.n; ++i) {
-      const int w = st.off[i + 1] - st.off[i];
-      n += (w + cols - 1) / cols;
-    }
-    if (n <= kMaxChunks) break;
-    cols *= 2;
-  }
-  ct.n = 0;
-  for (int i = 0; i < st.n; ++i) {
-    ct.per_slice[i] = 0;
-    ct.first[i] = ct.n;
-    for (int c = st.off[i]; c < st.off[i + 1]; c += cols) {
-      ct.slice[ct.n] = i;
-      ct.c0[ct.n] = c;
-      ct.c1[ct.n] = min(c + cols, st.off[i + 1]);
-      ++ct.n;
-      ++ct.per_slice[i];
-    }
-  }
+  const ChunkTable ct = make_chunks(st, R);
   const int KP = k_parts(in);
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
   const int64_t n_shrink = slots8 * st.n * KP;
@@ -690,6 +902,68 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
     hipLaunchKernelGGL((k_apply_fused<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,    \
                        stream, x, y, T, in, st, a, b, slots, R, token_order, indptr, ranks,     \
                        scalings, ct, (int)n_shrink, (int)n_expand, KP, part, pairs, spin_limit);  \
+  } while (0)
+  switch (rt) {
+    case 1: LAUNCH(1); break;
+    case 2: LAUNCH(2); break;
+    case 4: LAUNCH(4); break;
+    case 8: LAUNCH(8); break;
+    default: LAUNCH(16); break;
+  }
+#undef LAUNCH
+  return hipGetLastError();
+}
+
+
+hipError_t launch_decode_shrink(const void* x, int T, int in, const void* a, int slots, int S,
+                                int R, const int32_t* token_order, const int32_t* indptr,
+                                const int32_t* ranks, float* h, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int64_t grid = 8 * (int64_t)((slots + 7) / 8) * S;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int rt = rt_bucket(R);
+  const size_t lds = lds_bytes(rt, kNW);
+#define LAUNCH(RTV)                                                                             \
+  do {                                                                                          \
+    if (lds > 65536) {                                                                          \
+      hipError_t e = hipFuncSetAttribute((const void*)k_decode_shrink<RTV, kNW>,                \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+      if (e != hipSuccess) return e;                                                            \
+    }                                                                                           \
+    hipLaunchKernelGGL((k_decode_shrink<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,  \
+                       stream, x, T, in, a, slots, S, R, token_order, indptr, ranks, h);         \
+  } while (0)
+  switch (rt) {
+    case 1: LAUNCH(1); break;
+    case 2: LAUNCH(2); break;
+    case 4: LAUNCH(4); break;
+    case 8: LAUNCH(8); break;
+    default: LAUNCH(16); break;
+  }
+#undef LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_expand(void* y, int T, const SliceTable& st, const float* h,
+                                const void* b, int slots, int R, const int32_t* token_order,
+                                const int32_t* indptr, const int32_t* ranks,
+                                const float* scalings, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const ChunkTable ct = make_chunks(st, R);
+  const int64_t grid = 8 * (int64_t)((slots + 7) / 8) * ct.n;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int rt = rt_bucket(R);
+  const size_t lds = lds_bytes(rt, kNW);
+#define LAUNCH(RTV)                                                                             \
+  do {                                                                                          \
+    if (lds > 65536) {                                                                          \
+      hipError_t e = hipFuncSetAttribute((const void*)k_decode_expand<RTV, kNW>,                \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+      if (e != hipSuccess) return e;                                                            \
+    }                                                                                           \
+    hipLaunchKernelGGL((k_decode_expand<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,  \
+                       stream, y, T, st, h, b, slots, R, token_order, indptr, ranks, scalings,   \
+                       ct);                                                                     \
   } while (0)
   switch (rt) {
     case 1: LAUNCH(1); break;

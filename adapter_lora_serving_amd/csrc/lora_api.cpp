@@ -108,17 +108,23 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(x) || !aligned16(a) || !aligned16(h)) return LORA_ERR_ALIGNMENT;
   if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
-  // per-segment choice on the device: the VALU kernel takes segments of at
-  // most kLongSegment tokens, the MFMA kernel the longer ones
+  // per-segment choice on the device. bf16: segments of at most
+  // kLongSegment tokens on the decode tiles, longer ones on the SGMV tiles,
+  // and the VALU kernel writes only the zeros; otherwise (fp32, or sizes the
+  // MFMA kernels do not take) the VALU kernel computes every segment.
   SliceTable none;
   none.n = 1;
   none.off[0] = 0;
   none.off[1] = 16;
-  const bool mfma = lora::sgmv_supported(dtype, none, R, (int)T, (int)in_features);
+  const bool mfma = lora::sgmv_supported(dtype, none, R, (int)T, (int)in_features) &&
+                    lora::fused_supported(dtype, none, R, (int)T, (int)in_features);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
                                      token_order, slot_indptr, ranks, h,
-                                     mfma ? lora::kLongSegment : lora::kNoMaxSeg, s);
+                                     mfma ? 0 : lora::kNoMaxSeg, s);
+  if (e == hipSuccess && mfma)
+    e = lora::launch_decode_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                   token_order, slot_indptr, ranks, h, s);
   if (e == hipSuccess && mfma)
     e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
                                  token_order, slot_indptr, ranks, h, nullptr, 1, s);
@@ -153,14 +159,22 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
   if (!y || !h || !b || !scalings) return LORA_ERR_INVALID_ARG;
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(y) || !aligned16(h) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
-  const bool mfma = lora::sgmv_supported(dtype, tab, R, (int)T, 8);
+  // bf16: segments of at most kLongSegment tokens on the decode tiles,
+  // longer ones on the SGMV tiles; otherwise the VALU kernel takes all
+  const bool mfma = lora::sgmv_supported(dtype, tab, R, (int)T, 8) &&
+                    lora::fused_supported(dtype, tab, R, (int)T, 8);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
-                                     slot_indptr, ranks, scalings,
-                                     mfma ? lora::kLongSegment : lora::kNoMaxSeg, s);
-  if (e == hipSuccess && mfma)
-    e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr, ranks,
-                                 scalings, s);
+  hipError_t e = hipSuccess;
+  if (mfma) {
+    e = lora::launch_decode_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                   ranks, scalings, s);
+    if (e == hipSuccess)
+      e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                   ranks, scalings, s);
+  } else {
+    e = lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                            ranks, scalings, lora::kNoMaxSeg, s);
+  }
   return hip_status(e);
 }
 

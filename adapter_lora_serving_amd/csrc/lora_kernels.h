@@ -78,6 +78,18 @@ size_t counter_bytes(int slots, int S);
 size_t fused_partial_bytes(int slots, int S, int R, int in);
 // with_long: the fused kernel also takes segments longer than 16 tokens
 // (16-token blocks over every column); otherwise it leaves them to SGMV.
+// Standalone bf16 shrink / expand for segments of at most 16 tokens on the
+// decode tiles (MFMA): lora_shrink writes h's columns below the rank of those
+// tokens (the zeros come from launch_shrink with max_seg 0), lora_expand
+// reads h from memory. Supported where fused_supported() holds.
+hipError_t launch_decode_shrink(const void* x, int T, int in, const void* a, int slots, int S,
+                                int R, const int32_t* token_order, const int32_t* indptr,
+                                const int32_t* ranks, float* h, hipStream_t stream);
+hipError_t launch_decode_expand(void* y, int T, const SliceTable& st, const float* h,
+                                const void* b, int slots, int R, const int32_t* token_order,
+                                const int32_t* indptr, const int32_t* ranks,
+                                const float* scalings, hipStream_t stream);
+
 hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const SliceTable& st,
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,

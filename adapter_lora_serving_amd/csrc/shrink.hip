@@ -164,7 +164,9 @@ hipError_t launch_shrink(int dtype, const void* x, int T, int in, const void* a,
                          const int32_t* ranks, float* h, int max_seg, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // upper bound of compute items: sum over slots of S*ceil(r/8)*ceil(n/8)
-  const int64_t n_compute = (int64_t)S * ((R + kRG - 1) / kRG) * ((T + kTG - 1) / kTG + slots);
+  // (none when max_seg is 0: then only the zeros are written)
+  const int64_t n_compute =
+      max_seg > 0 ? (int64_t)S * ((R + kRG - 1) / kRG) * ((T + kTG - 1) / kTG + slots) : 0;
   const int64_t n_zero = ((int64_t)T * S * R + 255) / 256;
   const int64_t grid = n_compute + n_zero;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
