@@ -215,7 +215,10 @@ template <int NT, int NW, class XRow>
 __device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
                                                XRow xrow_of, int s0, int s1, f32x4* acc,
                                                int m, int kg, int w) {
-  constexpr int U = NT <= 1 ? 8 : NT <= 2 ? 4 : NT <= 4 ? 2 : 1;   // K steps in flight
+  // K steps in flight per wave; 2 or more below 16 tiles, so the two
+  // 64-byte halves of a 128-byte line of a row are read by the same wave
+  // (16 tiles would not fit the registers twice)
+  constexpr int U = NT <= 1 ? 8 : NT <= 2 ? 4 : NT <= 8 ? 2 : 1;
   int st0 = s0 + w * U;
   if (st0 >= s1) return;
   bf16x8 av[U][NT];
@@ -294,6 +297,106 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&acc)[RT]
     for (int ii = 0; ii < 4; ++ii) dst[(4 * kg + ii) * RP + nt * 16 + m] = acc[nt][ii];
 }
 
+// Loads of group g of a chunk's expand tiles: wave w takes tiles
+// w + NW*(g*PT + u), u < PT; B ranks at or past r and tiles past the chunk
+// read as zeros (kOOB), y rows of padding tokens too.
+template <int RT, int NW, int PT>
+__device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R, int r, int lo,
+                                                  int ntiles, bool live, uint32_t yrow, int g,
+                                                  s16x4 (&bv)[PT][RT], u32x2 (&yv)[PT], int m,
+                                                  int kg, int w) {
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int tile = w + NW * (g * PT + u);
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      const int kk = ks * 16 + kg * 4;
+      const uint32_t off = (tile < ntiles && kk < r)
+                               ? ((uint32_t)(lo + tile * 16 + m) * (uint32_t)R + kk) * 2u
+                               : kOOB;
+      bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int tile = w + NW * (g * PT + u);
+    yv[u] = bload8(y_r, (live && tile < ntiles) ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
+                                                : kOOB);
+  }
+}
+
+// Products and y update of group g from its loaded tiles.
+template <int RT, int NW, int PT>
+__device__ __forceinline__ void expand_group(rsrc_t y_r, int r, int lo, int ntiles, bool live,
+                                             uint32_t yrow, int g, const s16x4 (&bv)[PT][RT],
+                                             const u32x2 (&yv)[PT], const s16x4 (&hb)[RT],
+                                             const s16x4 (&lb)[RT], int kg, int w) {
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int tile = w + NW * (g * PT + u);
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < RT; ++ks) {
+      if (ks * 16 >= r) break;
+      const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
+      o = mfma_k16(b4, hb[ks], o);
+      o = mfma_k16(b4, lb[ks], o);
+    }
+    const uint32_t off = (live && tile < ntiles)
+                             ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
+                             : kOOB;
+    const u32x2 yy = yv[u];
+    bstore8(y_r, off,
+            u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
+                  pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
+  }
+}
+
+// Expand of a whole chunk once hhi / hlo hold the block's h: group 0 is
+// already loaded (bv0, yv0); each later group's loads are issued before the
+// products of the group before it (two register sets in turn), so a wide
+// chunk costs one load latency, not one per group.
+template <int RT, int NW, int PT>
+__device__ __forceinline__ void expand_chunk(rsrc_t b_r, rsrc_t y_r, int R, int r, int lo,
+                                             int ntiles, bool live, uint32_t yrow,
+                                             s16x4 (&bv0)[PT][RT], u32x2 (&yv0)[PT],
+                                             const uint16_t* hhi, const uint16_t* hlo, int m,
+                                             int kg, int w) {
+  constexpr int RPS = RT * 16 + 4;
+  s16x4 hb[RT], lb[RT];
+#pragma unroll
+  for (int ks = 0; ks < RT; ++ks) {
+    hb[ks] = *(const s16x4*)(hhi + m * RPS + ks * 16 + kg * 4);
+    lb[ks] = *(const s16x4*)(hlo + m * RPS + ks * 16 + kg * 4);
+  }
+  const int ngroups = (ntiles + NW * PT - 1) / (NW * PT);
+  if constexpr (RT <= 2) {
+    // small ranks: a decode chunk is one group (NW * PT tiles); a wider one
+    // (a tuning override) takes its further groups one after another
+    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, 0, bv0, yv0, hb, lb, kg, w);
+    for (int g = 1; g < ngroups; ++g) {
+      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g, bv0, yv0, m, kg,
+                                    w);
+      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g, bv0, yv0, hb, lb, kg, w);
+    }
+    return;
+  }
+  s16x4 bv1[PT][RT];
+  u32x2 yv1[PT];
+  for (int g = 0; g < ngroups; g += 2) {
+    if (g + 1 < ngroups)
+      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g + 1, bv1, yv1, m,
+                                    kg, w);
+    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g, bv0, yv0, hb, lb, kg, w);
+    if (g + 1 < ngroups) {
+      if (g + 2 < ngroups)
+        load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g + 2, bv0, yv0, m,
+                                      kg, w);
+      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g + 1, bv1, yv1, hb, lb, kg, w);
+    }
+  }
+}
+
 // Shrink piece (s, i, kp).
 template <int RT, int NW>
 __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, int r, int seg0,
@@ -345,29 +448,11 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
 
-  // B tiles first (no dependence on the token id), then the y rows
+  // group 0 of the chunk: B tiles, then the y rows (which need the token id)
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * u;
-#pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      const int kk = ks * 16 + kg * 4;
-      const uint32_t off = (tile < ntiles && kk < r)
-                               ? ((uint32_t)(lo + tile * 16 + m) * (uint32_t)R + kk) * 2u
-                               : kOOB;
-      bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
-    }
-  }
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * u;
-    yv[u] = bload8(d.y_r, (live && tile < ntiles)
-                              ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
-                              : kOOB);
-  }
+  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, 0, bv, yv, m, kg, w);
 
   if (tid == 0) {
     const int base = __hip_atomic_load(&pair->y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -413,50 +498,8 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   }
   __syncthreads();
 
-  s16x4 hb[RT], lb[RT];
-#pragma unroll
-  for (int ks = 0; ks < RT; ++ks) {
-    hb[ks] = *(const s16x4*)(hhi + m * RPS + ks * 16 + kg * 4);
-    lb[ks] = *(const s16x4*)(hlo + m * RPS + ks * 16 + kg * 4);
-  }
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * u;
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      if (ks * 16 >= r) break;
-      const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
-      o = mfma_k16(b4, hb[ks], o);
-      o = mfma_k16(b4, lb[ks], o);
-    }
-    const uint32_t off = (live && tile < ntiles)
-                             ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
-                             : kOOB;
-    const u32x2 yy = yv[u];
-    bstore8(d.y_r, off,
-            u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
-                  pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
-  }
-  // columns beyond the tiles held in registers (chunks wider than NW*PT*16)
-  for (int tile = w + NW * PT; tile < ntiles; tile += NW) {
-    const int c = lo + tile * 16;
-    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      if (ks * 16 >= r) break;
-      const int kk = ks * 16 + kg * 4;
-      const uint32_t boff = kk < r ? ((uint32_t)(c + m) * (uint32_t)R + kk) * 2u : kOOB;
-      const s16x4 b4 = mask_b4(__builtin_bit_cast(s16x4, bload8(b_r, boff)), kk, r);
-      o = mfma_k16(b4, hb[ks], o);
-      o = mfma_k16(b4, lb[ks], o);
-    }
-    const uint32_t off = live ? yrow + (uint32_t)(c + 4 * kg) * 2u : kOOB;
-    const u32x2 yy = bload8(d.y_r, off);
-    bstore8(d.y_r, off,
-            u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
-                  pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
-  }
+  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, bv, yv, hhi, hlo, m, kg,
+                           w);
 }
 
 // ---------------------------------------------------------------------------
@@ -519,28 +562,7 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
 
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
-  auto load_group = [&](int g) {
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int tile = w + NW * (g * PT + u);
-#pragma unroll
-      for (int ks = 0; ks < RT; ++ks) {
-        const int kk = ks * 16 + kg * 4;
-        const uint32_t off = (tile < ntiles && kk < r)
-                                 ? ((uint32_t)(lo + tile * 16 + m) * (uint32_t)R + kk) * 2u
-                                 : kOOB;
-        bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int tile = w + NW * (g * PT + u);
-      yv[u] = bload8(d.y_r, (live && tile < ntiles)
-                                ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
-                                : kOOB);
-    }
-  };
-  load_group(0);
+  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, 0, bv, yv, m, kg, w);
   if (w == 0 && kg == 0) tok[m] = live ? t : -1;
   __syncthreads();
   // h rows: scaled, split into bf16 hi + lo (ranks at or past r read as 0)
@@ -561,35 +583,8 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
   }
   __syncthreads();
 
-  s16x4 hb[RT], lb[RT];
-#pragma unroll
-  for (int ks = 0; ks < RT; ++ks) {
-    hb[ks] = *(const s16x4*)(hhi + m * RPS + ks * 16 + kg * 4);
-    lb[ks] = *(const s16x4*)(hlo + m * RPS + ks * 16 + kg * 4);
-  }
-  const int ngroups = (ntiles + NW * PT - 1) / (NW * PT);
-  for (int g = 0; g < ngroups; ++g) {
-    if (g > 0) load_group(g);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int tile = w + NW * (g * PT + u);
-      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < RT; ++ks) {
-        if (ks * 16 >= r) break;
-        const s16x4 b4 = mask_b4(bv[u][ks], ks * 16 + kg * 4, r);
-        o = mfma_k16(b4, hb[ks], o);
-        o = mfma_k16(b4, lb[ks], o);
-      }
-      const uint32_t off = (live && tile < ntiles)
-                               ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
-                               : kOOB;
-      const u32x2 yy = yv[u];
-      bstore8(d.y_r, off,
-              u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
-                    pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
-    }
-  }
+  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, bv, yv, hhi, hlo, m, kg,
+                           w);
 }
 
 }  // namespace
@@ -600,8 +595,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     const void* __restrict__ a_, const void* __restrict__ b_, int slots, int R,
     const int32_t* __restrict__ token_order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, const float* __restrict__ scalings, ChunkTable ct,
-    int n_shrink, int n_expand, int KP, float* __restrict__ part, int2* __restrict__ pairs,
-    int spin_limit) {
+    int n_shrink, int n_expand, int nclass, int KP, float* __restrict__ part,
+    int2* __restrict__ pairs, int spin_limit) {
   using L = Lds<RT, NW>;
   constexpr int RP = RT * 16;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -622,19 +617,30 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   if (bid < n_shrink + n_expand) {
     // decode pieces; block bid = 8*k + xcd runs on XCD `xcd`, and every piece
     // of slot s = 8*q + xcd is placed there, so they share that XCD's L2
+    // With nclass > 1 each region (shrink, expand) is laid out once per rank
+    // class, largest ranks first, and a piece runs in the pass of its slot's
+    // class: the dispatcher, which starts blocks in order, then begins the
+    // longest pieces first.
     const bool is_shrink = bid < n_shrink;
-    const int b = is_shrink ? bid : bid - n_shrink;
+    const int per_slot = is_shrink ? S * KP : ct.n;
+    int b = is_shrink ? bid : bid - n_shrink;
+    int cls = 0;
+    if (nclass > 1) {
+      const int pass = 8 * ((slots + 7) / 8) * per_slot;
+      cls = b / pass;
+      b -= cls * pass;
+    }
     const int xcd = b & 7;
     const int k = b >> 3;
-    const int per_slot = is_shrink ? S * KP : ct.n;
     const int q = k / per_slot;
     const int rem = k - q * per_slot;
     const int s = q * 8 + xcd;
     if (s >= slots) return;
     int seg0, n;
-    segment_of(indptr, s, T, seg0, n);
+    segment_of(indptr, s, T, seg0, n);   // issued with the rank load, not after it
     const int r = clamp_rank(ranks[s], R);
-    if (n == 0 || r == 0 || n > kMT) return;
+    if (r == 0 || n == 0 || n > kMT) return;
+    if (nclass > 1 && cls != (2 * r > R ? 0 : 4 * r > R ? 1 : 2)) return;
     const int i = is_shrink ? rem / KP : ct.slice[rem];
     DecodeArgs d;
     d.x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
@@ -880,8 +886,10 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const ChunkTable ct = make_chunks(st, R);
   const int KP = k_parts(in);
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
-  const int64_t n_shrink = slots8 * st.n * KP;
-  const int64_t n_expand = slots8 * ct.n;
+  // rank classes (largest first) where ranks differ enough to matter
+  const int nclass = rt_bucket(R) >= 4 ? 3 : 1;
+  const int64_t n_shrink = nclass * slots8 * st.n * KP;
+  const int64_t n_expand = nclass * slots8 * ct.n;
   const int64_t n_prefill = with_long ? (T + kMT - 1) / kMT + slots : 0;
   const int64_t grid = n_shrink + n_expand + n_prefill;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -901,7 +909,8 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
     }                                                                                           \
     hipLaunchKernelGGL((k_apply_fused<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,    \
                        stream, x, y, T, in, st, a, b, slots, R, token_order, indptr, ranks,     \
-                       scalings, ct, (int)n_shrink, (int)n_expand, KP, part, pairs, spin_limit);  \
+                       scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part, pairs,      \
+                       spin_limit);                                                             \
   } while (0)
   switch (rt) {
     case 1: LAUNCH(1); break;
