@@ -636,9 +636,12 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     const int rem = k - q * per_slot;
     const int s = q * 8 + xcd;
     if (s >= slots) return;
+    // the three loads are issued together; reading the rank first keeps the
+    // compiler from waiting on the segment bounds before requesting it
+    const int r_raw = __builtin_nontemporal_load(ranks + s);
     int seg0, n;
-    segment_of(indptr, s, T, seg0, n);   // issued with the rank load, not after it
-    const int r = clamp_rank(ranks[s], R);
+    segment_of(indptr, s, T, seg0, n);
+    const int r = clamp_rank(r_raw, R);
     if (r == 0 || n == 0 || n > kMT) return;
     if (nclass > 1 && cls != (2 * r > R ? 0 : 4 * r > R ? 1 : 2)) return;
     const int i = is_shrink ? rem / KP : ct.slice[rem];
