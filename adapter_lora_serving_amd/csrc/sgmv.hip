@@ -7,14 +7,13 @@
 // scalings[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T); the slice
 // layout follows mstar.model.components.linear, FusedColumnLinear.
 //
-// Shrink item: (slot, block of 32 tokens of its segment, slice). Four waves:
-//   wave w computes token tile (w & 1) against rank tiles of half (w >> 1).
-//   K advances in chunks of 64: the x block [32 x 64] and A rows [RP x 64]
-//   are staged in LDS (double buffered, rows padded by 16 bytes so the
-//   MFMA operand reads hit distinct banks) with one 16-byte buffer load per
-//   thread and piece; rows of A at or past the rank lie outside the A
-//   resource and read as zeros without a memory access. Each wave writes its
-//   16 x 16 tiles of h (fp32) directly: no reduction across waves.
+// Shrink item: (slot, block of 128 tokens of its segment, slice, K part).
+//   Eight waves; wave w owns token tile w against every rank tile. Its x
+//   rows go straight from HBM into registers a few 64-element chunks ahead;
+//   A's chunk is shared through a double-buffered LDS tile. Rows of A at or
+//   past the rank lie outside the A resource and read as zeros without a
+//   memory access. With several K parts each item writes a partial h and a
+//   second kernel sums the parts.
 // Expand item: (slot, block of 64 tokens, 256 output columns of one slice).
 //   The block's h rows are scaled and split into bf16 hi + lo in LDS; every
 //   wave prefetches its 4 column tiles of B and y in one round trip, then
@@ -63,16 +62,16 @@ constexpr int kBMs = 128;
 constexpr int kD = 4;
 
 template <int RT>
-__global__ __launch_bounds__(512) void k_sgmv_shrink(const void* __restrict__ x_, int T, int in,
-                                                     const void* __restrict__ a_, int slots, int S,
-                                                     int R, const int32_t* __restrict__ order,
-                                                     const int32_t* __restrict__ indptr,
-                                                     const int32_t* __restrict__ ranks,
-                                                     float* __restrict__ hout, int kparts,
-                                                     int64_t part_stride) {
+// Six waves per SIMD (three workgroups per CU) keep a prefill batch's items
+// resident in one round, so no item starts after the first round ends.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k_sgmv_shrink(
+    const void* __restrict__ x_, int T, int in, const void* __restrict__ a_, int slots, int S,
+    int R, const int32_t* __restrict__ order, const int32_t* __restrict__ indptr,
+    const int32_t* __restrict__ ranks, float* __restrict__ hout, int kparts,
+    int64_t part_stride) {
   constexpr int RP = RT * 16;
   constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
-  constexpr int D = RT >= 8 ? 2 : kD;          // chunks in flight (register budget)
+  constexpr int D = RT >= 8 ? 2 : RT >= 4 ? 3 : kD;   // chunks in flight (register budget)
   __shared__ int scratch[24];
   __shared__ int tok[kBMs];
   __shared__ __attribute__((aligned(16))) char as[2][RP * kRowB];
@@ -447,7 +446,7 @@ bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in) {
 
 int sgmv_kparts(int in) {
   const int kp = in / 1024;
-  return kp < 1 ? 1 : kp > 8 ? 8 : kp;
+  return kp < 1 ? 1 : kp > 16 ? 16 : kp;
 }
 
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
