@@ -240,11 +240,13 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
 // expand
 // ---------------------------------------------------------------------------
 // Item: (slot, block of 64 tokens, 256 output columns of one slice). Wave w
-// owns columns [lo + 64w, lo + 64w + 64) for the 64 tokens. The MFMA result
-// comes out as 4 columns of one token per lane; it is staged through a
-// per-wave LDS tile so that y is read and written row-major, 16 bytes per
-// lane: one instruction covers 8 token rows x 128 contiguous bytes, full
-// cache lines, so HBM never sees partial-line writes.
+// owns columns [lo + 64w, lo + 64w + 64) for the 64 tokens. Every global
+// access is 16 bytes per lane: B rows as 8 consecutive ranks (two
+// 16x16x16 products per 32 ranks), h rows as 4 consecutive ranks, and y
+// row-major. The MFMA result comes out as 4 columns of one token per lane;
+// it is staged through a per-wave LDS tile so that y is read and written
+// row-major: one instruction covers 8 token rows x 128 contiguous bytes,
+// full cache lines, so HBM never sees partial-line writes.
 template <int RT>
 __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int T, SliceTable st,
                                                      const float* __restrict__ h,
@@ -254,10 +256,13 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
                                                      const int32_t* __restrict__ ranks,
                                                      const float* __restrict__ scalings) {
   constexpr int RP = RT * 16;
-  constexpr int RPS = RP + 4;
+  constexpr int RPS = RP + 8;         // LDS h row (bf16), 16-byte aligned rows
   constexpr int MT = kBMe / 16;       // token tiles
   constexpr int TPW = kCC / 16 / 4;   // column tiles per wave (4: 64 columns)
   constexpr int SRW = 64 + 4;         // staged row (floats), padded
+  constexpr bool K32 = RT >= 2;       // 32 ranks per step (8 per lane)
+  constexpr int KS = K32 ? RT / 2 : RT;
+  constexpr int KW = K32 ? 32 : 16;
   __shared__ int scratch[24];
   __shared__ int tok[kBMe];
   __shared__ __attribute__((aligned(16))) uint16_t hhi[kBMe * RPS];
@@ -311,18 +316,24 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
                                (uint32_t)out * (uint32_t)R * 2u);
   const int ntiles = (hi - lo) >> 4;
   const int cw = lo + w * 64;         // this wave's first column
-  const int ntr = (r + 15) / 16;      // rank tiles holding ranks below r
-  s16x4 bv[TPW][RT];
+  const int ntr = (r + KW - 1) / KW;  // rank steps holding ranks below r
+  // lane (m, kg) holds B[column][ranks kk, kk + KW/4) of each of its tiles
+  u32x4 bq[TPW][KS];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tile = w * TPW + u;
 #pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      const int kk = ks * 16 + kg * 4;
-      bv[u][ks] = __builtin_bit_cast(
-          s16x4, bload8(b_r, (tile < ntiles && kk < r)
-                                 ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
-                                 : kOOB));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kk = ks * KW + kg * (KW / 4);
+      const uint32_t off = (tile < ntiles && kk < r)
+                               ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
+                               : kOOB;
+      if constexpr (K32) {
+        bq[u][ks] = bload16(b_r, off);
+      } else {
+        const u32x2 v = bload8(b_r, off);
+        bq[u][ks] = u32x4{v.x, v.y, 0u, 0u};
+      }
     }
   }
   if (tid < kBMe) tok[tid] = tid < ntok ? tv : -1;
@@ -344,63 +355,89 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
                                    : kOOB);
     }
 
-  // h rows of the block (only ranks below r are read), scaled, split hi + lo;
-  // all of a thread's loads are issued before any is used
+  // h rows of the block, 4 ranks per load (ranks at or past r are set to
+  // zero; they are the block's own h columns, not adapter weights), scaled
+  // and split hi + lo; all of a thread's loads are issued before any is used
   const float scale = scalings[s];
   const int SR = S * R;
-  constexpr int HL = kBMe * RP / 256;   // h values per thread
+  constexpr int RQ = RP / 4;                    // 16-byte pieces per h row
+  constexpr int HQ = (kBMe * RQ + 255) / 256;   // pieces per thread
   const rsrc_t h_r = make_rsrc(h, (uint32_t)T * (uint32_t)SR * 4u);
-  float hv[HL];
+  u32x4 hv[HQ];
 #pragma unroll
-  for (int k = 0; k < HL; ++k) {
+  for (int k = 0; k < HQ; ++k) {
     const int idx = tid + 256 * k;
-    const int q = idx / RP;
-    const int j = idx - q * RP;
-    const int t = tok[q];
-    hv[k] = __uint_as_float(
-        bload4(h_r, (t >= 0 && j < r) ? ((uint32_t)t * (uint32_t)SR + i * R + j) * 4u : kOOB));
+    const int q = idx / RQ;
+    const int j = (idx - q * RQ) * 4;
+    const int t = q < kBMe ? tok[q] : -1;
+    hv[k] = bload16(h_r, (t >= 0 && j < r) ? ((uint32_t)t * (uint32_t)SR + i * R + j) * 4u
+                                           : kOOB);
   }
 #pragma unroll
-  for (int k = 0; k < HL; ++k) {
+  for (int k = 0; k < HQ; ++k) {
     const int idx = tid + 256 * k;
-    const int q = idx / RP;
-    const int j = idx - q * RP;
-    const float v = hv[k] * scale;
-    const uint32_t hb = to_bf16_bits(v);
-    const uint32_t lb = to_bf16_bits(v - __uint_as_float(hb << 16));
-    hhi[q * RPS + j] = (uint16_t)hb;
-    hlo[q * RPS + j] = (uint16_t)lb;
+    const int q = idx / RQ;
+    const int j = (idx - q * RQ) * 4;
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = (j + e < r) ? __uint_as_float(hv[k][e]) * scale : 0.f;
+      hb[e] = to_bf16_bits(v);
+      lb[e] = to_bf16_bits(v - __uint_as_float(hb[e] << 16));
+    }
+    if (q < kBMe) {
+      *(u32x2*)(hhi + q * RPS + j) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+      *(u32x2*)(hlo + q * RPS + j) = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+    }
   }
   __syncthreads();
 
-  // ranks past r in a live group are never used
+  // ranks past r in a live step are never used
 #pragma unroll
   for (int u = 0; u < TPW; ++u)
 #pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
-      const int kk = ks * 16 + kg * 4;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kk = ks * KW + kg * (KW / 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bv[u][ks][e] = (kk + e < r) ? bv[u][ks][e] : (short)0;
+      for (int e = 0; e < (K32 ? 4 : 2); ++e) {
+        const uint32_t mlo = (kk + 2 * e < r) ? 0xffffu : 0u;
+        const uint32_t mhi = (kk + 2 * e + 1 < r) ? 0xffff0000u : 0u;
+        bq[u][ks][e] &= mlo | mhi;
+      }
     }
 
+  auto half = [](u32x4 v, int p) {   // bf16 quadruple p (0 or 1) of a 16-byte piece
+    return __builtin_bit_cast(s16x4, p ? u32x2{v.z, v.w} : u32x2{v.x, v.y});
+  };
   float* sw = stage[w];
 #pragma unroll
   for (int q = 0; q < MT; ++q) {
-    s16x4 hb[RT], lb[RT];
+    u32x4 hq[KS], lq[KS];
 #pragma unroll
-    for (int ks = 0; ks < RT; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       if (ks >= ntr) break;
-      hb[ks] = *(const s16x4*)(hhi + (q * 16 + m) * RPS + ks * 16 + kg * 4);
-      lb[ks] = *(const s16x4*)(hlo + (q * 16 + m) * RPS + ks * 16 + kg * 4);
+      const int off = (q * 16 + m) * RPS + ks * KW + kg * (KW / 4);
+      if constexpr (K32) {
+        hq[ks] = *(const u32x4*)(hhi + off);
+        lq[ks] = *(const u32x4*)(hlo + off);
+      } else {
+        const u32x2 a = *(const u32x2*)(hhi + off);
+        const u32x2 c = *(const u32x2*)(hlo + off);
+        hq[ks] = u32x4{a.x, a.y, 0u, 0u};
+        lq[ks] = u32x4{c.x, c.y, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < RT; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         if (ks >= ntr) break;
-        o = mfma_k16(bv[u][ks], hb[ks], o);
-        o = mfma_k16(bv[u][ks], lb[ks], o);
+#pragma unroll
+        for (int p = 0; p < (K32 ? 2 : 1); ++p) {
+          o = mfma_k16(half(bq[u][ks], p), half(hq[ks], p), o);
+          o = mfma_k16(half(bq[u][ks], p), half(lq[ks], p), o);
+        }
       }
       // o[ii] = delta[token m][column 16u + 4kg + ii]
       *(f32x4*)(sw + m * SRW + u * 16 + kg * 4) = o;
