@@ -180,24 +180,32 @@ __device__ __forceinline__ SlotItem locate_item(int item, int slots, CountFn cou
 }
 
 // As locate_item, with the item chosen from the total: item = pick(total)
-// (the same value in every thread; negative for none). One pass over the
-// slots (each count evaluated once when slots <= blockDim.x), so a
-// workgroup learns its item after a single round of loads. The thread that
-// finds the item calls stash(slot, scratch + 20) to leave up to four ints of
-// per-slot data (read them after the call, before scratch is reused).
-template <typename CountFn, typename PickFn, typename StashFn>
-__device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, CountFn count,
-                                                  int* scratch /* >= 24 ints LDS */,
-                                                  StashFn stash) {
+// (the same value in every thread; negative for none). Each slot's values
+// are loaded once by info(s, v) (three ints: segment begin, length, rank)
+// and its item count is count_of(v). When slots <= blockDim.x every thread
+// holds at most one slot and keeps its values in registers, so a workgroup
+// learns its item, and the item's slot values, after a single round of
+// loads; they are left in scratch[20..22] (read them after the call, before
+// scratch is reused).
+template <typename PickFn, typename InfoFn, typename CountFn>
+__device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, InfoFn info,
+                                                  CountFn count_of,
+                                                  int* scratch /* >= 24 ints LDS */) {
   const int nthreads = blockDim.x;
   const int chunk = (slots + nthreads - 1) / nthreads;
   const int s0 = threadIdx.x * chunk;
   const int s1 = min(slots, s0 + chunk);
+  int v0[3] = {0, 0, 0};   // values of slot s0
   int local = 0;
   int first = 0;
   for (int s = s0; s < s1; ++s) {
-    const int c = count(s);
-    if (s == s0) first = c;
+    int v[3];
+    info(s, v);
+    const int c = count_of(v);
+    if (s == s0) {
+      first = c;
+      v0[0] = v[0]; v0[1] = v[1]; v0[2] = v[2];
+    }
     local += c;
   }
   int total = 0;
@@ -208,11 +216,15 @@ __device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, CountF
   if (item >= 0 && item >= excl && item < excl + local) {
     int run = excl;
     for (int s = s0; s < s1; ++s) {
-      const int c = s == s0 ? first : count(s);
+      int v[3] = {v0[0], v0[1], v0[2]};
+      if (s != s0) info(s, v);
+      const int c = s == s0 ? first : count_of(v);
       if (item < run + c) {
         scratch[18] = s;
         scratch[19] = item - run;
-        stash(s, scratch + 20);   // per-slot values the caller wants (up to 4 ints)
+        scratch[20] = v[0];
+        scratch[21] = v[1];
+        scratch[22] = v[2];
         break;
       }
       run += c;

@@ -79,18 +79,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
-  auto count = [&](int s) -> int {
-    int b0, n;
-    segment_of(indptr, s, T, b0, n);
-    return (n > kLong && clamp_rank(ranks[s], R) > 0) ? S * kparts * ((n + kBMs - 1) / kBMs)
-                                                      : 0;
-  };
   const SlotItem it = locate_picked(
-      [&](int total) { return xcd_item(blockIdx.x, total); }, slots, count, scratch,
+      [&](int total) { return xcd_item(blockIdx.x, total); }, slots,
       [&](int ss, int* v) {
         segment_of(indptr, ss, T, v[0], v[1]);
         v[2] = clamp_rank(ranks[ss], R);
-      });
+      },
+      [&](const int* v) {
+        return (v[1] > kLong && v[2] > 0) ? S * kparts * ((v[1] + kBMs - 1) / kBMs) : 0;
+      },
+      scratch);
   if (it.slot < 0) return;
   const int s = it.slot;
   const int seg0 = scratch[20];
@@ -277,17 +275,16 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   // column chunks: slice i holds ceil(w_i / kCC) chunks
   int nck = 0;
   for (int i = 0; i < S; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
-  auto count = [&](int s) -> int {
-    int b0, n;
-    segment_of(indptr, s, T, b0, n);
-    return (n > kLong && clamp_rank(ranks[s], R) > 0) ? nck * ((n + kBMe - 1) / kBMe) : 0;
-  };
   const SlotItem it = locate_picked(
-      [&](int total) { return xcd_item(blockIdx.x, total); }, slots, count, scratch,
+      [&](int total) { return xcd_item(blockIdx.x, total); }, slots,
       [&](int ss, int* v) {
         segment_of(indptr, ss, T, v[0], v[1]);
         v[2] = clamp_rank(ranks[ss], R);
-      });
+      },
+      [&](const int* v) {
+        return (v[1] > kLong && v[2] > 0) ? nck * ((v[1] + kBMe - 1) / kBMe) : 0;
+      },
+      scratch);
   if (it.slot < 0) return;
   const int s = it.slot;
   const int seg0 = scratch[20];
