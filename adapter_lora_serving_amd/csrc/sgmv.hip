@@ -19,9 +19,12 @@
 //   wave prefetches its 4 column tiles of B and y in one round trip, then
 //   y^T tile = B_tile . H^T with two v_mfma_f32_16x16x16_bf16 per 16 ranks
 //   and 4 token tiles, one rounding of y.
-// Items are numbered XCD by XCD (block b runs on XCD b % 8 and takes item
-// (b % 8) * ceil(N/8) + b / 8), so consecutive blocks of one slot share an
-// XCD's L2 for A (shrink) or B (expand).
+// Items run in block order (blocks are dealt to the 8 XCDs round robin), and
+// consecutive items sweep along token rows: an expand item's column chunks
+// are innermost, so the workgroups resident at one time read and write y in
+// long row-major runs; the chunk count per token block is padded to a
+// multiple of 8 so chunk ck always runs on XCD ck % 8 and its B tile stays in
+// that XCD's L2. A shrink item's K parts are innermost for the same reason.
 #include "lora_common.h"
 #include "lora_kernels.h"
 
@@ -37,13 +40,9 @@ constexpr int kKC = 64;       // K elements per staged chunk
 constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
 
 
-// XCD-contiguous item index of block b among n items; -1 past the end.
-__device__ __forceinline__ int xcd_item(int b, int n) {
-  const int per = (n + 7) / 8;
-  const int k = b >> 3;
-  if (k >= per) return -1;
-  const int it = (b & 7) * per + k;
-  return it < n ? it : -1;
+// Item of block b among n items; -1 past the end.
+__device__ __forceinline__ int block_item(int n) {
+  return (int)blockIdx.x < n ? (int)blockIdx.x : -1;
 }
 
 }  // namespace
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int lane = lane_id();
   const int w = wave_id();
   const SlotItem it = locate_picked(
-      [&](int total) { return xcd_item(blockIdx.x, total); }, slots,
+      [&](int total) { return block_item(total); }, slots,
       [&](int ss, int* v) {
         segment_of(indptr, ss, T, v[0], v[1]);
         v[2] = clamp_rank(ranks[ss], R);
@@ -95,10 +94,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int n = scratch[21];
   const int r = scratch[22];
   const int nmb = (n + kBMs - 1) / kBMs;
-  const int mb = it.local % nmb;
-  const int rest = it.local / nmb;
-  const int kp = rest % kparts;
-  const int i = rest / kparts;
+  const int kp = it.local % kparts;
+  const int rest = it.local / kparts;
+  const int mb = rest % nmb;
+  const int i = rest / nmb;
   const int ntok = min(kBMs, n - mb * kBMs);
   // the token ids are the oldest loads in flight; the first A chunks (which
   // do not depend on them) are issued next, then the ids are waited for
@@ -275,14 +274,15 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   // column chunks: slice i holds ceil(w_i / kCC) chunks
   int nck = 0;
   for (int i = 0; i < S; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
+  const int nck8 = (nck + 7) & ~7;   // chunk slots per token block (padding items idle)
   const SlotItem it = locate_picked(
-      [&](int total) { return xcd_item(blockIdx.x, total); }, slots,
+      [&](int total) { return block_item(total); }, slots,
       [&](int ss, int* v) {
         segment_of(indptr, ss, T, v[0], v[1]);
         v[2] = clamp_rank(ranks[ss], R);
       },
       [&](const int* v) {
-        return (v[1] > kLong && v[2] > 0) ? nck * ((v[1] + kBMe - 1) / kBMe) : 0;
+        return (v[1] > kLong && v[2] > 0) ? nck8 * ((v[1] + kBMe - 1) / kBMe) : 0;
       },
       scratch);
   if (it.slot < 0) return;
@@ -290,9 +290,9 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   const int seg0 = scratch[20];
   const int n = scratch[21];
   const int r = scratch[22];
-  const int nmb = (n + kBMe - 1) / kBMe;
-  const int mb = it.local % nmb;
-  int ck = it.local / nmb;
+  const int mb = it.local / nck8;
+  int ck = it.local % nck8;
+  if (ck >= nck) return;
   int i = 0;
   for (; i < S; ++i) {
     const int c = (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
@@ -519,7 +519,7 @@ hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float*
   if (T <= kLong) return hipSuccess;
   int nck = 0;
   for (int i = 0; i < st.n; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
-  const int64_t items = (int64_t)nck * ((T + kBMe - 1) / kBMe + slots);
+  const int64_t items = (int64_t)((nck + 7) & ~7) * ((T + kBMe - 1) / kBMe + slots);
   const int64_t grid = 8 * ((items + 7) / 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
 #define L(RTV)                                                                                 \
