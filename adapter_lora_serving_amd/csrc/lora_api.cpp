@@ -127,7 +127,8 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
                                    token_order, slot_indptr, ranks, h, s);
   if (e == hipSuccess && mfma)
     e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                 token_order, slot_indptr, ranks, h, nullptr, 1, s);
+                                 token_order, slot_indptr, ranks, h, nullptr, 1,
+                                 lora::kLongSegment, s);
   return hip_status(e);
 }
 
@@ -170,7 +171,7 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
                                    ranks, scalings, s);
     if (e == hipSuccess)
       e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
-                                   ranks, scalings, s);
+                                   ranks, scalings, lora::kLongSegment, s);
   } else {
     e = lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
                             ranks, scalings, lora::kNoMaxSeg, s);
@@ -215,23 +216,25 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
                                       partial_bytes(slots, num_slices, R, in_features));
   if (lora::fused_supported(dtype, tab, R, (int)T, (int)in_features)) {
     // The host picks the kernel family from T only (fixed per captured
-    // graph): small batches run everything in the fused kernel; larger ones
-    // leave segments longer than 16 tokens to the SGMV shrink and expand,
-    // which write and read their h in the workspace. Which segment goes
-    // where is decided on the device from slot_indptr.
-    const bool small = T < kFusedAllBelowT;
-    hipError_t e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
-                                            token_order, slot_indptr, ranks, scalings, workspace,
-                                            small, s);
-    if (e == hipSuccess && !small) {
+    // graph): small batches run everything in the fused kernel (decode
+    // pieces for segments of at most 16 tokens, 16-token prefill items for
+    // longer ones); larger batches run every segment through the SGMV
+    // shrink and expand, which write and read their h in the workspace.
+    // There the few-token segments are pure weight streaming, which the
+    // SGMV tiles' shared, deeper loads serve better than the decode pieces.
+    hipError_t e;
+    if (T < kFusedAllBelowT) {
+      e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
+                                   token_order, slot_indptr, ranks, scalings, workspace, true, s);
+    } else {
       const int kp = lora::sgmv_kparts((int)in_features);
       float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);
       e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                   token_order, slot_indptr, ranks, h, parts, kp, s);
+                                   token_order, slot_indptr, ranks, h, parts, kp, 0, s);
+      if (e == hipSuccess)
+        e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                     ranks, scalings, 0, s);
     }
-    if (e == hipSuccess && !small)
-      e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
-                                   ranks, scalings, s);
     return hip_status(e);
   }
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,

@@ -51,7 +51,8 @@ hipError_t launch_expand(int dtype, void* y, int T, const SliceTable& st, const 
                          const int32_t* indptr, const int32_t* ranks, const float* scalings,
                          int max_seg, hipStream_t stream);
 
-// SGMV (bf16 MFMA) shrink / expand over segments longer than kLongSegment.
+// SGMV (bf16 MFMA) shrink / expand over the segments longer than min_len
+// tokens (kLongSegment next to the decode tiles; 0 takes every segment).
 constexpr int kLongSegment = 16;
 bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in);
 // kparts > 1 splits K: the parts go to `parts` (kparts * T * S * R floats)
@@ -60,10 +61,11 @@ int sgmv_kparts(int in);
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
                               int R, const int32_t* order, const int32_t* indptr,
                               const int32_t* ranks, float* h, float* parts, int kparts,
-                              hipStream_t stream);
+                              int min_len, hipStream_t stream);
 hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float* h, const void* b,
                               int slots, int R, const int32_t* order, const int32_t* indptr,
-                              const int32_t* ranks, const float* scalings, hipStream_t stream);
+                              const int32_t* ranks, const float* scalings, int min_len,
+                              hipStream_t stream);
 
 // Fused shrink + expand (bf16, MFMA). fused_supported() tells whether the
 // shapes qualify (bf16, every slice width a multiple of 16, R <= 256, every

@@ -1,6 +1,8 @@
-// Segment-tiled (SGMV) shrink and expand on bf16 MFMA, for slot segments
-// longer than 16 tokens, where the per-slot products are real dense
-// contractions.
+// Segment-tiled (SGMV) shrink and expand on bf16 MFMA, for the slot segments
+// longer than a given length (min_len): 16 tokens next to the decode tiles,
+// or 0 (every segment) for a large batch, where the long segments' products
+// are real dense contractions and the short ones stream their adapter
+// weights through the same tiles.
 //
 // Follows the mstar lora.backend page: LoraBackend.shrink (h[t] =
 // x[t] @ a[slot(t)]^T) and LoraBackend.expand_fused (y[t, slice i] +=
@@ -33,7 +35,6 @@ namespace lora {
 namespace {
 
 
-constexpr int kLong = 16;     // segments longer than this take the SGMV path
 constexpr int kBMe = 64;      // tokens per expand item
 constexpr int kCC = 256;      // output columns per expand item
 constexpr int kKC = 64;       // K elements per staged chunk
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const void* __restrict__ x_, int T, int in, const void* __restrict__ a_, int slots, int S,
     int R, const int32_t* __restrict__ order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, float* __restrict__ hout, int kparts,
-    int64_t part_stride) {
+    int64_t part_stride, int min_len) {
   constexpr int RP = RT * 16;
   constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
   constexpr int D = RT >= 8 ? 2 : RT >= 4 ? 3 : kD;   // chunks in flight (register budget)
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
         v[2] = clamp_rank(ranks[ss], R);
       },
       [&](const int* v) {
-        return (v[1] > kLong && v[2] > 0) ? S * kparts * ((v[1] + kBMs - 1) / kBMs) : 0;
+        return (v[1] > min_len && v[2] > 0) ? S * kparts * ((v[1] + kBMs - 1) / kBMs) : 0;
       },
       scratch);
   if (it.slot < 0) return;
@@ -207,13 +208,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
 }
 
 // h[t, :] = sum over kp (in order) of part[kp][t, :], for the tokens of
-// segments longer than kLong (the only rows the parts hold).
+// segments longer than min_len (the only rows the parts hold).
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int kparts,
                                                    int64_t part_stride, float* __restrict__ h,
                                                    int T, int SR, int slots, int R,
                                                    const int32_t* __restrict__ order,
                                                    const int32_t* __restrict__ indptr,
-                                                   const int32_t* __restrict__ ranks) {
+                                                   const int32_t* __restrict__ ranks,
+                                                   int min_len) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (position, 4 columns)
   const int cq = SR / 4;
   if (g >= (int64_t)T * cq) return;
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   if (s >= slots) return;
   int b0, n;
   segment_of(indptr, s, T, b0, n);
-  if (n <= kLong || clamp_rank(ranks[s], R) == 0) return;
+  if (n <= min_len || clamp_rank(ranks[s], R) == 0) return;
   const int64_t off = (int64_t)token_at(order, p, T) * SR + c;
   f32x4 v = *(const f32x4*)(part + off);
   for (int k = 1; k < kparts; ++k) {
@@ -251,7 +253,8 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
                                                      int R, const int32_t* __restrict__ order,
                                                      const int32_t* __restrict__ indptr,
                                                      const int32_t* __restrict__ ranks,
-                                                     const float* __restrict__ scalings) {
+                                                     const float* __restrict__ scalings,
+                                                     int min_len) {
   constexpr int RP = RT * 16;
   constexpr int RPS = RP + 8;         // LDS h row (bf16), 16-byte aligned rows
   constexpr int MT = kBMe / 16;       // token tiles
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
         v[2] = clamp_rank(ranks[ss], R);
       },
       [&](const int* v) {
-        return (v[1] > kLong && v[2] > 0) ? nck8 * ((v[1] + kBMe - 1) / kBMe) : 0;
+        return (v[1] > min_len && v[2] > 0) ? nck8 * ((v[1] + kBMe - 1) / kBMe) : 0;
       },
       scratch);
   if (it.slot < 0) return;
@@ -486,8 +489,8 @@ int sgmv_kparts(int in) {
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
                               int R, const int32_t* order, const int32_t* indptr,
                               const int32_t* ranks, float* h, float* parts, int kparts,
-                              hipStream_t stream) {
-  if (T <= kLong) return hipSuccess;   // no segment can be long
+                              int min_len, hipStream_t stream) {
+  if (T <= min_len) return hipSuccess;   // no segment can be long enough
   if (kparts < 1 || (kparts > 1 && !parts)) return hipErrorInvalidValue;
   const int64_t stride = (int64_t)T * S * R;
   const int64_t items = (int64_t)S * kparts * ((T + kBMs - 1) / kBMs + slots);
@@ -496,7 +499,7 @@ hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int s
   float* dst = kparts > 1 ? parts : h;
 #define L(RTV)                                                                                 \
   hipLaunchKernelGGL(k_sgmv_shrink<RTV>, dim3((unsigned)grid), dim3(512), 0, stream, x, T, in, \
-                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride)
+                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len)
   switch (rt_of(R)) {
     case 1: L(1); break;
     case 2: L(2); break;
@@ -509,14 +512,15 @@ hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int s
   if (e != hipSuccess || kparts == 1) return e;
   const int64_t n = (int64_t)T * (S * R / 4);
   hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, parts,
-                     kparts, stride, h, T, S * R, slots, R, order, indptr, ranks);
+                     kparts, stride, h, T, S * R, slots, R, order, indptr, ranks, min_len);
   return hipGetLastError();
 }
 
 hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float* h, const void* b,
                               int slots, int R, const int32_t* order, const int32_t* indptr,
-                              const int32_t* ranks, const float* scalings, hipStream_t stream) {
-  if (T <= kLong) return hipSuccess;
+                              const int32_t* ranks, const float* scalings, int min_len,
+                              hipStream_t stream) {
+  if (T <= min_len) return hipSuccess;
   int nck = 0;
   for (int i = 0; i < st.n; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
   const int64_t items = (int64_t)((nck + 7) & ~7) * ((T + kBMe - 1) / kBMe + slots);
@@ -524,7 +528,7 @@ hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float*
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
 #define L(RTV)                                                                                 \
   hipLaunchKernelGGL(k_sgmv_expand<RTV>, dim3((unsigned)grid), dim3(256), 0, stream, y, T, st, \
-                     h, b, slots, R, order, indptr, ranks, scalings)
+                     h, b, slots, R, order, indptr, ranks, scalings, min_len)
   switch (rt_of(R)) {
     case 1: L(1); break;
     case 2: L(2); break;

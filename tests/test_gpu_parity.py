@@ -207,9 +207,13 @@ def test_poison_h_unread(k):
 
 
 def _custom(seed, *, T, in_f, out_slices, R, slots, ranks, dtype="bf16", dead=0.0,
-            scal=None):
+            scal=None, skew=0.0):
     rng = np.random.default_rng(seed)
-    ts = rng.integers(0, slots, size=T)
+    if skew > 0:   # slot k drawn with weight 1 / (k + 1)^skew: a few long segments, many short
+        p = 1.0 / np.arange(1, slots + 1) ** skew
+        ts = rng.choice(slots, size=T, p=p / p.sum())
+    else:
+        ts = rng.integers(0, slots, size=T)
     kill = rng.random(T) < dead
     ts[kill] = -1
     scal = rng.uniform(0.5, 2.0, size=slots) if scal is None else scal
@@ -241,6 +245,10 @@ EDGE = {
                           ranks=[32, 16, 5]),
     "ragged_k_rank128": dict(T=1100, in_f=776, out_slices=(256, 64, 64), R=128, slots=70,
                              ranks=[128, 64, 8, 100, 0] * 14),
+    # a large batch (every segment on the SGMV tiles) whose skewed slot mix
+    # leaves most segments a few tokens long
+    "large_skewed": dict(T=2048, in_f=1024, out_slices=(512, 128, 128), R=128, slots=96,
+                         ranks=[128, 64, 32, 16, 8, 0] * 16, skew=1.2, dead=0.02),
 }
 
 
