@@ -53,7 +53,7 @@ __device__ __forceinline__ int block_item(int n) {
 // ---------------------------------------------------------------------------
 // Item: (slot, block of 128 tokens, slice, K part). Eight waves, wave w owns
 // token tile w (16 tokens) against every rank tile, so its x rows are its own
-// (read straight into registers, D chunks ahead) and only A is shared: A's
+// (read into registers D chunks ahead) and only A is shared: A's
 // chunk [RP x 64] goes through a register ring D chunks ahead into a
 // double-buffered LDS tile. A is thus re-read from L2 once per 128 tokens.
 // With kparts > 1 each item writes its partial h to its own buffer
@@ -72,9 +72,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   constexpr int RP = RT * 16;
   constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
   constexpr int D = RT >= 8 ? 2 : RT >= 4 ? 3 : kD;   // chunks in flight (register budget)
+  // XL: x rows are loaded as 8 rows x 128 contiguous bytes per instruction
+  // and turned into the MFMA operand layout through a per-wave LDS tile
+  // (16 rows x 64 bytes per instruction otherwise); the tile's 18 KB would
+  // cost a workgroup per CU at the largest ranks, so those load directly
+  constexpr bool XL = RT <= 4;
   __shared__ int scratch[24];
   __shared__ int tok[kBMs];
   __shared__ __attribute__((aligned(16))) char as[2][RP * kRowB];
+  __shared__ __attribute__((aligned(16))) char xs[XL ? 8 : 1][XL ? 16 * kRowB : 16];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -136,16 +142,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   for (int d = 0; d < D; ++d) issue_a(d, d);
   if (tid < kBMs) tok[tid] = tid < ntok ? tv : -1;
   __syncthreads();
-  const int t = tok[w * 16 + m];
-  const uint32_t xrow = t >= 0 ? (uint32_t)t * rowG : kOOB;
+  // x rows of this lane: XL: rows xq and xq + 8 of the wave's 16 tokens,
+  // 16-byte piece xp of the chunk; else row m, pieces kg and 4 + kg
+  const int xq = lane >> 3;
+  const int xp = lane & 7;
+  uint32_t xrow[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int t = tok[w * 16 + (XL ? xq + 8 * hh : m)];
+    xrow[hh] = t >= 0 ? (uint32_t)t * rowG : kOOB;
+  }
   auto issue_x = [&](int slot, int c) {   // x loads of chunk c (relative) into ring slot
     const bool cv = c < nch;
     const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t e = (uint32_t)((cbeg + c) * kKC + ks * 32 + kg * 8);
-      xr[slot][ks] = bload16(x_r, (cv && xrow != kOOB && e < (uint32_t)in)
-                                      ? xrow + kb + (uint32_t)(ks * 32 + kg * 8) * 2u
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ke = XL ? xp * 8 : hh * 32 + kg * 8;   // element offset in the chunk
+      const uint32_t e = (uint32_t)((cbeg + c) * kKC + ke);
+      xr[slot][hh] = bload16(x_r, (cv && xrow[hh] != kOOB && e < (uint32_t)in)
+                                      ? xrow[hh] + kb + (uint32_t)ke * 2u
                                       : kOOB);
     }
   };
@@ -173,9 +188,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
       if (c < nch) {
         if (c + 1 < nch) stage((d + 1) % D, (c + 1) & 1);
         const char* ab = as[c & 1];
+        if constexpr (XL) {
+          *(u32x4*)(xs[w] + xq * kRowB + xp * 16) = xr[d][0];
+          *(u32x4*)(xs[w] + (xq + 8) * kRowB + xp * 16) = xr[d][1];
+          __builtin_amdgcn_wave_barrier();
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[d][ks]);
+          bf16x8 xa;
+          if constexpr (XL)
+            xa = __builtin_bit_cast(bf16x8,
+                                    *(const u32x4*)(xs[w] + m * kRowB + (ks * 32 + kg * 8) * 2));
+          else
+            xa = __builtin_bit_cast(bf16x8, xr[d][ks]);
 #pragma unroll
           for (int nt = 0; nt < RT; ++nt) {
             if (nt >= ntr) break;   // rank tiles past r hold only zeros
