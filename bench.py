@@ -67,7 +67,8 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the kernel sources as they are now; else None."""
+    taken on the kernel sources as they are now; else None. `workload` is the
+    workload name, with the target appended for a multi-target workload."""
     p = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -277,7 +278,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(wl.name),
+            "traffic": measured_traffic(wl.name if len(wl.targets) == 1
+                                        else f"{wl.name}_{tg.name}"),
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "avg_launch_us": round(ms_apply * 1e3, 3),
         },
