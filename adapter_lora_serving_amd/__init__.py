@@ -43,7 +43,8 @@ SIGNATURES = {
     "lora_version": (ctypes.c_char_p, []),
     "lora_build_addressing": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P,
-                                   _P, _P, _P]),
+                                   _P, _P, _P, _SZ, _P]),
+    "lora_shrink_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
     "lora_gather_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _P, _P,
                                           _P, _P, _P]),
     "lora_expand": (ctypes.c_int, [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P,
@@ -159,8 +160,13 @@ def shrink(x, a, addressing, ranks, num_slices: int = 1, out=None):
     R = SR // num_slices
     if out is None:
         out = torch.empty(T, SR, dtype=torch.float32, device=dev)
+    # K-part workspace for long segments (from torch's caching allocator;
+    # its contents need no initialisation)
+    nws = int(lib().lora_shrink_workspace_bytes(T, in_f, num_slices, R))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     st = lib().lora_shrink(_dtype_code(x), _ptr(x), T, in_f, _ptr(a), slots, num_slices, R,
-                           _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(out), _stream(dev))
+                           _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(out),
+                           _ptr(ws), nws, _stream(dev))
     _check(st, "lora_shrink")
     return out
 

@@ -63,8 +63,10 @@ size_t partial_bytes(int32_t slots, int32_t S, int32_t R, int64_t in) {
   return (lora::fused_partial_bytes(slots, S, R, (int)in) + 255) & ~(size_t)255;
 }
 
-// Batches smaller than this run every segment in the fused kernel.
-constexpr int64_t kFusedAllBelowT = 1024;
+// Batches of at least this many tokens (bf16) run every segment on the SGMV
+// tiles; smaller ones use the fused kernel (apply) or the decode tiles for
+// segments of at most kLongSegment tokens (shrink, expand).
+constexpr int64_t kLargeBatch = 1024;
 
 }  // namespace
 
@@ -94,10 +96,20 @@ lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t 
                                                   slot_indptr, (hipStream_t)stream));
 }
 
+size_t lora_shrink_workspace_bytes(int64_t T, int64_t in_features, int32_t num_slices,
+                                   int32_t R) {
+  if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
+      R > 256 || in_features < 1 || in_features > kMaxI32)
+    return 0;
+  const int kp = lora::sgmv_kparts((int)in_features);
+  return kp > 1 ? ws_h_bytes(T, num_slices, R) * kp : 0;
+}
+
 lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features, const void* a,
                         int32_t slots, int32_t num_slices, int32_t R,
                         const int32_t* token_order, const int32_t* slot_indptr,
-                        const int32_t* ranks, float* h, void* stream) {
+                        const int32_t* ranks, float* h, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   lora_status st = check_common(dtype, T, slots, R);
   if (st != LORA_OK) return st;
   if (num_slices < 1 || num_slices > lora::kMaxSlices) return LORA_ERR_UNSUPPORTED;
@@ -108,10 +120,19 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(x) || !aligned16(a) || !aligned16(h)) return LORA_ERR_ALIGNMENT;
   if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
-  // per-segment choice on the device. bf16: segments of at most
-  // kLongSegment tokens on the decode tiles, longer ones on the SGMV tiles,
-  // and the VALU kernel writes only the zeros; otherwise (fp32, or sizes the
-  // MFMA kernels do not take) the VALU kernel computes every segment.
+  // K parts of the long segments when the caller lends a workspace
+  int kparts = 1;
+  if (workspace) {
+    const size_t need = lora_shrink_workspace_bytes(T, in_features, num_slices, R);
+    if (workspace_bytes < need) return LORA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+    if (need > 0) kparts = lora::sgmv_kparts((int)in_features);
+  }
+  // per-segment choice on the device. bf16: in a small batch, segments of at
+  // most kLongSegment tokens on the decode tiles and longer ones on the SGMV
+  // tiles, in a large batch every segment on the SGMV tiles, and the VALU
+  // kernel writes only the zeros; otherwise (fp32, or sizes the MFMA kernels
+  // do not take) the VALU kernel computes every segment.
   SliceTable none;
   none.n = 1;
   none.off[0] = 0;
@@ -122,13 +143,15 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
                                      token_order, slot_indptr, ranks, h,
                                      mfma ? 0 : lora::kNoMaxSeg, s);
-  if (e == hipSuccess && mfma)
+  const bool large = T >= kLargeBatch;
+  if (e == hipSuccess && mfma && !large)
     e = lora::launch_decode_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
                                    token_order, slot_indptr, ranks, h, s);
   if (e == hipSuccess && mfma)
     e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                 token_order, slot_indptr, ranks, h, nullptr, 1,
-                                 lora::kLongSegment, s);
+                                 token_order, slot_indptr, ranks, h,
+                                 kparts > 1 ? static_cast<float*>(workspace) : nullptr, kparts,
+                                 large ? 0 : lora::kLongSegment, s);
   return hip_status(e);
 }
 
@@ -160,18 +183,21 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
   if (!y || !h || !b || !scalings) return LORA_ERR_INVALID_ARG;
   if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
   if (!aligned16(y) || !aligned16(h) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
-  // bf16: segments of at most kLongSegment tokens on the decode tiles,
-  // longer ones on the SGMV tiles; otherwise the VALU kernel takes all
+  // bf16: in a small batch, segments of at most kLongSegment tokens on the
+  // decode tiles and longer ones on the SGMV tiles, in a large batch every
+  // segment on the SGMV tiles; otherwise the VALU kernel takes all
   const bool mfma = lora::sgmv_supported(dtype, tab, R, (int)T, 8) &&
                     lora::fused_supported(dtype, tab, R, (int)T, 8);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (mfma) {
-    e = lora::launch_decode_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
-                                   ranks, scalings, s);
+    const bool large = T >= kLargeBatch;
+    if (!large)
+      e = lora::launch_decode_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                     ranks, scalings, s);
     if (e == hipSuccess)
       e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
-                                   ranks, scalings, lora::kLongSegment, s);
+                                   ranks, scalings, large ? 0 : lora::kLongSegment, s);
   } else {
     e = lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
                             ranks, scalings, lora::kNoMaxSeg, s);
@@ -223,7 +249,7 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
     // There the few-token segments are pure weight streaming, which the
     // SGMV tiles' shared, deeper loads serve better than the decode pieces.
     hipError_t e;
-    if (T < kFusedAllBelowT) {
+    if (T < kLargeBatch) {
       e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
                                    token_order, slot_indptr, ranks, scalings, workspace, true, s);
     } else {

@@ -109,13 +109,30 @@ lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t 
  * shrink_reference (zeros where the expand does not read).
  * Writes ALL of h [T, num_slices*R]: every entry the expand does not read
  * (dead tokens, rank-0 slots, columns at or past a slot's rank) is 0.
- * Segments long enough to form a dense contraction run on bf16 MFMA, short
- * ones on a VALU dot-product path; the choice is made on the device.
+ * bf16: in a batch of fewer than 1024 tokens, segments of at most 16 tokens
+ * run on the MFMA decode tiles and longer ones on the MFMA segment tiles; in
+ * a larger batch every segment runs on the segment tiles; a VALU kernel
+ * writes the zeros. fp32 runs on the VALU kernel. Which segment goes where
+ * is decided on the device.
+ * workspace (device, optional): with at least
+ * lora_shrink_workspace_bytes(...) bytes, 256-byte aligned, the long
+ * segments' products are split along in_features into parts that are summed
+ * in a fixed order (the same h bit for bit on every call, and more
+ * workgroups for a large batch); NULL (with workspace_bytes 0) runs them in
+ * one part. Contents need no initialisation; calls sharing one workspace
+ * must not overlap in time. A non-NULL workspace that is too small is
+ * LORA_ERR_WORKSPACE.
  */
 lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features,
                         const void* a, int32_t slots, int32_t num_slices, int32_t R,
                         const int32_t* token_order, const int32_t* slot_indptr,
-                        const int32_t* ranks, float* h, void* stream);
+                        const int32_t* ranks, float* h, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_shrink can use for these sizes; 0 when it would not
+ * split (or on bad input, which the call itself reports). */
+size_t lora_shrink_workspace_bytes(int64_t T, int64_t in_features, int32_t num_slices,
+                                   int32_t R);
 
 /*
  * lora_gather_shrink: h[t, j] = a[slot(t), j, ids[t]] for j < rank(slot(t)).

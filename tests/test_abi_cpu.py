@@ -56,12 +56,12 @@ def _slices(*w):
 def test_shrink_validation(lib):
     f = lib.lora_shrink
     args = dict(dtype=1, x=A16, T=4, inf=64, a=A16, slots=2, S=1, R=16, order=A16, indptr=A16,
-                ranks=A16, h=A16, stream=None)
+                ranks=A16, h=A16, ws=None, wsb=0, stream=None)
 
     def call(**kw):
         d = {**args, **kw}
         return f(d["dtype"], d["x"], d["T"], d["inf"], d["a"], d["slots"], d["S"], d["R"],
-                 d["order"], d["indptr"], d["ranks"], d["h"], d["stream"])
+                 d["order"], d["indptr"], d["ranks"], d["h"], d["ws"], d["wsb"], d["stream"])
 
     assert call(dtype=7) == UNSUPPORTED
     assert call(T=-1) == INVALID
@@ -78,6 +78,13 @@ def test_shrink_validation(lib):
     assert call(x=MIS) == ALIGN
     assert call(inf=60) == ALIGN
     assert call(T=0, x=None, a=None, h=None) == OK    # nothing to do: no launch
+    # a lent workspace must hold the K parts and be 256-byte aligned
+    need = lib.lora_shrink_workspace_bytes(4, 4096, 1, 16)
+    assert need == 4 * 16 * 4 * 4                  # 4 parts of a [4, 16] float32 h
+    assert call(inf=4096, ws=A16, wsb=need - 1) == WORKSPACE
+    assert call(inf=4096, ws=A16 + 16, wsb=need) == ALIGN
+    assert lib.lora_shrink_workspace_bytes(4, 1024, 1, 16) == 0    # too shallow to split
+    assert lib.lora_shrink_workspace_bytes(-1, 4096, 1, 16) == 0   # bad input
 
 
 def test_expand_validation(lib):

@@ -138,13 +138,15 @@ def test_linear_parity_small(k, name, seed, fused):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("k,name", [(3, "gate_up"), (3, "down"), (5, None)])
-def test_linear_full_size_sampled(k, name):
+@pytest.mark.parametrize("fused", [True, False])
+def test_linear_full_size_sampled(k, name, fused):
     """Full-size configs; the oracle checks sampled rows: the first and last
-    token of every segment plus random ones."""
-    log(f"full-size config {k} {name}")
+    token of every segment plus random ones. Unfused, the shrink splits K
+    into parts in the workspace the binding lends it."""
+    log(f"full-size config {k} {name} fused={fused}")
     wl = W.make_config(k, 0)
     tg = wl.target(name)
-    _, _, y = GpuTarget(wl, tg).run(fused=True)
+    _, _, y = GpuTarget(wl, tg).run(fused=fused)
     yg = f64(y)
     order, indptr = O.build_addressing(wl.token_slot, wl.slots)
     pick = set()
@@ -157,6 +159,36 @@ def test_linear_full_size_sampled(k, name):
     sub = W.take_tokens(wl, idx)
     _, y_ref = O.run_target(sub, sub.target(name))
     assert_tol(yg[idx], y_ref, f"config {k} {name} sampled")
+
+
+def test_shrink_k_parts():
+    """lora_shrink with a workspace (K split into parts, summed in order)
+    against the oracle, against the same call without one (one part), and
+    against itself (bit for bit)."""
+    log("shrink K parts")
+    t = torch()
+    wl = W.make_config(3, 1, T=1024, in_features=4096, inter=1024)
+    tg = wl.target("gate_up")
+    g = GpuTarget(wl, tg)
+    addr = g.addressing()
+    assert L.lib().lora_shrink_workspace_bytes(wl.T, 4096, 2, wl.R) > 0
+    h1 = L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices)
+    h2 = L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices)
+    h0 = t.empty_like(h1)
+    st = L.lib().lora_shrink(1, g.x.data_ptr(), wl.T, 4096, g.a.data_ptr(), wl.slots,
+                             tg.num_slices, wl.R, addr.token_order.data_ptr(),
+                             addr.slot_indptr.data_ptr(), g.ranks.data_ptr(), h0.data_ptr(),
+                             None, 0, t.cuda.current_stream().cuda_stream)
+    assert st == 0
+    t.cuda.synchronize()
+    assert t.equal(h1, h2)
+    h_ref, _ = O.run_target(wl, tg)
+    unread = unread_mask(wl, tg.num_slices)
+    for h in (h1, h0):
+        hg = f64(h)
+        assert np.all(hg[unread] == 0.0)
+        np.testing.assert_allclose(hg[~unread], h_ref[~unread], rtol=1e-3, atol=1e-3)
+    np.testing.assert_allclose(f64(h1), f64(h0), rtol=1e-5, atol=1e-5)
 
 
 def test_decode_full_fused_vs_unfused():
