@@ -80,19 +80,23 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   const int t0 = min(T, w * per);
   const int t1 = min(T, t0 + per);
   int* row = cnt + w * S1;
+  const int ng = (t1 - t0 + kWave - 1) / kWave;   // this wave's groups (uniform)
+  // the first kCache groups are unrolled (their matches stay in registers,
+  // indexed at compile time); any further ones loop
   GroupMatch cache[kCache];
 #pragma unroll
-  for (int c = 0; c < kCache; ++c) cache[c] = GroupMatch{-1, 0, 0, false};
-  {
-    int c = 0;
-    for (int base = t0; base < t1; base += kWave, ++c) {
-      const int t = base + lane;
-      const GroupMatch g = match_group(token_slot, t, t < t1, slots, nbits);
-      if (g.leader) row[g.key] += g.count;   // distinct keys: no two leaders collide
+  for (int c = 0; c < kCache; ++c) {
+    const int t = t0 + c * kWave + lane;
+    cache[c] = c < ng ? match_group(token_slot, t, t < t1, slots, nbits)
+                      : GroupMatch{-1, 0, 0, false};
+  }
 #pragma unroll
-      for (int cc = 0; cc < kCache; ++cc)
-        if (cc == c) cache[cc] = g;
-    }
+  for (int c = 0; c < kCache; ++c)   // distinct keys: no two leaders of a group collide
+    if (cache[c].leader) row[cache[c].key] += cache[c].count;
+  for (int c = kCache; c < ng; ++c) {
+    const int t = t0 + c * kWave + lane;
+    const GroupMatch g = match_group(token_slot, t, t < t1, slots, nbits);
+    if (g.leader) row[g.key] += g.count;
   }
   __syncthreads();
 
@@ -129,24 +133,19 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   __syncthreads();
 
   // stable scatter: only wave w touches row w of cnt
-  {
-    int c = 0;
-    for (int base = t0; base < t1; base += kWave, ++c) {
-      const int t = base + lane;
-      GroupMatch g;
-      if (c < kCache) {
+  auto scatter = [&](const GroupMatch& g, int t) {
+    int pos = 0;
+    if (t < t1) pos = row[g.key] + g.rank;
+    __builtin_amdgcn_wave_barrier();
+    if (g.leader) row[g.key] += g.count;
+    if (t < t1) token_order[pos] = t;
+  };
 #pragma unroll
-        for (int cc = 0; cc < kCache; ++cc)
-          if (cc == c) g = cache[cc];
-      } else {
-        g = match_group(token_slot, t, t < t1, slots, nbits);
-      }
-      int pos = 0;
-      if (t < t1) pos = row[g.key] + g.rank;
-      __builtin_amdgcn_wave_barrier();
-      if (g.leader) row[g.key] += g.count;
-      if (t < t1) token_order[pos] = t;
-    }
+  for (int c = 0; c < kCache; ++c)
+    if (c < ng) scatter(cache[c], t0 + c * kWave + lane);
+  for (int c = kCache; c < ng; ++c) {
+    const int t = t0 + c * kWave + lane;
+    scatter(match_group(token_slot, t, t < t1, slots, nbits), t);
   }
 }
 
