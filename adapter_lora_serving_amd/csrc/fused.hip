@@ -884,7 +884,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              bool with_long, hipStream_t stream) {
+                              hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const ChunkTable ct = make_chunks(st, R);
   const int KP = k_parts(in);
@@ -893,7 +893,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int nclass = rt_bucket(R) >= 4 ? 3 : 1;
   const int64_t n_shrink = nclass * slots8 * st.n * KP;
   const int64_t n_expand = nclass * slots8 * ct.n;
-  const int64_t n_prefill = with_long ? (T + kMT - 1) / kMT + slots : 0;
+  const int64_t n_prefill = (T + kMT - 1) / kMT + slots;
   const int64_t grid = n_shrink + n_expand + n_prefill;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   int2* pairs = (int2*)workspace;

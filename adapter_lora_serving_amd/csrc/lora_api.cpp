@@ -251,7 +251,7 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
     hipError_t e;
     if (T < kLargeBatch) {
       e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
-                                   token_order, slot_indptr, ranks, scalings, workspace, true, s);
+                                   token_order, slot_indptr, ranks, scalings, workspace, s);
     } else {
       const int kp = lora::sgmv_kparts((int)in_features);
       float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);

@@ -78,8 +78,6 @@ bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in);
 // path's h.
 size_t counter_bytes(int slots, int S);
 size_t fused_partial_bytes(int slots, int S, int R, int in);
-// with_long: the fused kernel also takes segments longer than 16 tokens
-// (16-token blocks over every column); otherwise it leaves them to SGMV.
 // Standalone bf16 shrink / expand for segments of at most 16 tokens on the
 // decode tiles (MFMA): lora_shrink writes h's columns below the rank of those
 // tokens (the zeros come from launch_shrink with max_seg 0), lora_expand
@@ -92,10 +90,12 @@ hipError_t launch_decode_expand(void* y, int T, const SliceTable& st, const floa
                                 const int32_t* indptr, const int32_t* ranks,
                                 const float* scalings, hipStream_t stream);
 
+// The fused kernel for a small batch: decode pieces for segments of at most
+// 16 tokens, 16-token prefill items over every column for longer ones.
 hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const SliceTable& st,
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              bool with_long, hipStream_t stream);
+                              hipStream_t stream);
 
 }  // namespace lora
