@@ -191,6 +191,54 @@ def test_shrink_k_parts():
     np.testing.assert_allclose(f64(h1), f64(h0), rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.slow
+def test_y_over_2gib_fallback():
+    """A y of more than 2 GiB: the MFMA kernels' 32-bit buffer offsets cannot
+    reach it, so the host picks the VALU kernels (64-bit offsets). Sampled
+    rows, both paths, against the oracle; the y0 = 0 rows are built on the
+    device (the batch is too large to draw on the host)."""
+    t = torch()
+    T, in_f, out, R, slots = 18000, 64, 60000, 16, 4
+    log(f"y over 2 GiB: T={T} out={out}")
+    assert T * out * 2 >= 2 ** 31
+    rng = np.random.default_rng(7)
+    ranks = np.array([16, 8, 0, 16], np.int32)
+    scal = rng.uniform(0.5, 2.0, size=slots).astype(np.float32)
+    ts = rng.integers(0, slots, size=T).astype(np.int32)
+    ts[rng.random(T) < 0.02] = -1
+    # A and B for the full output width (x and y0 of this one-token draw unused)
+    base = W.make_workload(name="over_2gib", dtype="bf16", T=1, in_features=in_f,
+                           out_slices=(out,), R=R, slots=slots, ranks=ranks, scalings=scal,
+                           token_slot=ts[:1], seed=7, rng=rng, y0_zero=True)
+    tb = base.targets[0]
+    x = W.f32_to_bf16_bits(rng.standard_normal((T, in_f)).astype(np.float32))
+    xd, ad, bd = dev(x, "bf16"), dev(tb.a, "bf16"), dev(tb.b, "bf16")
+    rk = t.from_numpy(ranks).to("cuda:0")
+    sc = t.from_numpy(scal).to("cuda:0")
+    addr = L.build_addressing(t.from_numpy(ts).to("cuda:0"), slots)
+    y1 = t.zeros(T, out, dtype=t.bfloat16, device="cuda:0")
+    L.apply_linear_(xd, y1, ad, bd, addr, rk, sc, (out,))
+    y2 = t.zeros(T, out, dtype=t.bfloat16, device="cuda:0")
+    h = L.shrink(xd, ad, addr, rk, 1)
+    L.expand_(h, bd, addr, rk, sc, y2, (out,))
+    t.cuda.synchronize()
+    order, indptr = O.build_addressing(ts, slots)
+    pick = {0, T - 1}
+    for s in range(slots):
+        if indptr[s + 1] > indptr[s]:
+            pick.update([int(order[indptr[s]]), int(order[indptr[s + 1] - 1])])
+    pick.update(rng.choice(T, size=24, replace=False).tolist())
+    idx = np.array(sorted(pick))
+    sub = W.Workload(name="over_2gib", dtype="bf16", T=len(idx), R=R, slots=slots,
+                     ranks=ranks, scalings=scal, token_slot=ts[idx], seed=7)
+    sub.targets.append(W.Target(name="t0", in_features=in_f, out_slices=(out,), a=tb.a,
+                                b=tb.b, y0=np.zeros((len(idx), out), np.uint16), x=x[idx]))
+    _, y_ref = O.run_target(sub, sub.targets[0])
+    ii = t.from_numpy(idx).to("cuda:0")
+    assert_tol(f64(y1[ii]), y_ref, "over 2 GiB fused")
+    assert_tol(f64(y2[ii]), y_ref, "over 2 GiB unfused")
+
+
 def test_decode_full_fused_vs_unfused():
     """Config 2 (the decode workload) at full size, both paths, seeds 0-2."""
     for seed in range(3):
