@@ -5,7 +5,8 @@
 // The grouping is a stable counting sort keyed by slot, dead tokens (slot
 // outside [0, slots)) keyed after every live slot. One workgroup of up to 16
 // waves does the whole batch, with no host round trip, so a serving step can
-// be captured in a hipGraph:
+// be captured in a hipGraph (a batch of at most 1024 tokens over at most 63
+// slots takes the one-wave kernel below instead):
 //   1. wave w owns the contiguous token range [w*per, (w+1)*per); for every
 //      group of 64 tokens each lane finds the lanes holding the same key with
 //      one ballot per key bit (log2(slots+1) ballots, independent of how many
@@ -34,14 +35,11 @@ struct GroupMatch {
   bool leader;  // lowest lane with this key
 };
 
-__device__ __forceinline__ GroupMatch match_group(const int32_t* __restrict__ token_slot, int t,
-                                                  bool valid, int slots, int nbits) {
+// raw: the token's slot as stored (ignored when !valid)
+__device__ __forceinline__ GroupMatch match_raw(int raw, bool valid, int slots, int nbits) {
   GroupMatch g;
   int k = -1;
-  if (valid) {
-    const int s = token_slot[t];
-    k = (s >= 0 && s < slots) ? s : slots;
-  }
+  if (valid) k = (raw >= 0 && raw < slots) ? raw : slots;
   uint64_t eq = __ballot(valid);
   for (int b = 0; b < nbits; ++b) {
     const bool bit = (k >> b) & 1;
@@ -54,6 +52,11 @@ __device__ __forceinline__ GroupMatch match_group(const int32_t* __restrict__ to
   g.count = __popcll(eq);
   g.leader = valid && below == 0;
   return g;
+}
+
+__device__ __forceinline__ GroupMatch match_group(const int32_t* __restrict__ token_slot, int t,
+                                                  bool valid, int slots, int nbits) {
+  return match_raw(valid ? token_slot[t] : -1, valid, slots, nbits);
 }
 
 }  // namespace
@@ -149,6 +152,51 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
   }
 }
 
+// Small batches over at most 63 slots: one wave sorts the whole batch (G
+// groups of 64 tokens, all slots loaded at once) with no workgroup barrier.
+// Per group, each lane's offset within its key is the key's count so far
+// (an LDS histogram of 64 entries) plus its rank among equal keys in the
+// group; lane k then holds key k for the scan that gives slot_indptr, and
+// the scatter adds the key's start.
+template <int G>
+__global__ __launch_bounds__(64) void k_build_addressing_wave(
+    const int32_t* __restrict__ token_slot, int T, int slots, int32_t* __restrict__ token_order,
+    int32_t* __restrict__ slot_indptr) {
+  __shared__ int hist[kWave];
+  const int lane = lane_id();
+  const int nbits = 32 - __clz(slots);
+  int raw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    raw[g] = t < T ? token_slot[t] : -1;
+  }
+  hist[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  int key[G], off[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    const GroupMatch m = match_raw(raw[g], t < T, slots, nbits);
+    key[g] = m.key < 0 ? 0 : m.key;   // lanes past T: any valid index, never used
+    off[g] = hist[key[g]] + m.rank;
+    __builtin_amdgcn_wave_barrier();
+    if (m.leader) hist[m.key] += m.count;   // distinct keys: no two leaders collide
+    __builtin_amdgcn_wave_barrier();
+  }
+  const int c = lane <= slots ? hist[lane] : 0;
+  const int start = wave_inclusive_scan(c) - c;
+  if (lane <= slots) slot_indptr[lane] = start;
+  __builtin_amdgcn_wave_barrier();
+  hist[lane] = start;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    if (t < T) token_order[hist[key[g]] + off[g]] = t;
+  }
+}
+
 int addressing_waves(int64_t T, int slots) {
   int nw = (int)((T + kWave - 1) / kWave);
   if (nw < 1) nw = 1;
@@ -166,6 +214,24 @@ size_t addressing_lds_bytes(int nw, int slots) {
 hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
                                    int32_t* token_order, int32_t* slot_indptr,
                                    hipStream_t stream) {
+  if (slots + 1 <= kWave && T <= 16 * kWave) {
+    const int groups = (T + kWave - 1) / kWave;
+#define W(GV)                                                                                    \
+  hipLaunchKernelGGL(k_build_addressing_wave<GV>, dim3(1), dim3(kWave), 0, stream, token_slot, T, \
+                     slots, token_order, slot_indptr)
+    if (groups <= 1)
+      W(1);
+    else if (groups <= 2)
+      W(2);
+    else if (groups <= 4)
+      W(4);
+    else if (groups <= 8)
+      W(8);
+    else
+      W(16);
+#undef W
+    return hipGetLastError();
+  }
   const int nw = addressing_waves(T, slots);
   const size_t lds = addressing_lds_bytes(nw, slots);
   if (lds > 65536) {

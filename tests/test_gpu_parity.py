@@ -59,7 +59,10 @@ def test_addressing_configs(k, seed):
 
 @pytest.mark.parametrize("T,slots,dead", [(0, 4, 0.0), (1, 1, 0.0), (63, 3, 0.3), (64, 7, 0.5),
                                           (65, 2, 0.0), (1000, 1, 0.1), (5000, 300, 0.2),
-                                          (200, 5, 1.0), (8192, 8192, 0.05), (70000, 64, 0.01)])
+                                          (200, 5, 1.0), (8192, 8192, 0.05), (70000, 64, 0.01),
+                                          # edges of the one-wave kernel (T <= 1024, slots <= 63)
+                                          (1024, 63, 0.1), (1025, 63, 0.0), (300, 64, 0.2),
+                                          (129, 40, 0.5)])
 def test_addressing_edges(T, slots, dead):
     log(f"addressing T={T} slots={slots} dead={dead}")
     rng = np.random.default_rng(T + slots)
