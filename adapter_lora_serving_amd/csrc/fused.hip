@@ -1,4 +1,6 @@
-// Fused shrink + expand for bf16 targets (lora_apply_linear), on bf16 MFMA.
+// Fused shrink + expand for bf16 targets (lora_apply_linear) of a small
+// batch (fewer than 1024 tokens; larger batches run the segment-tiled
+// kernels), on bf16 MFMA.
 //
 // Follows the mstar lora.backend page, LoraBackend.apply_linear_ ("a backend
 // may fuse them"): the result is that of shrink (h = x @ A^T, per token's
@@ -13,9 +15,8 @@
 //    slice) prefetches its B tile and y rows, waits for the slice's KP
 //    partial tiles (a counter handoff, described below), adds them in a
 //    fixed order, and expands its chunk. No byte of A or B is read twice.
-//  * prefill items, for longer segments when the whole batch runs here:
-//    (slot, block of 16 tokens) over every slice and output column; h of the
-//    block stays in LDS.
+//  * prefill items, for longer segments: (slot, block of 16 tokens) over
+//    every slice and output column; h of the block stays in LDS.
 // Shrink: K is split across the 8 waves; each wave accumulates a 16x16 tile
 //   (tokens x A rows) per 16 rank rows on bf16 MFMA, and the waves' partial
 //   tiles are added in a fixed order through LDS. Rows of A at or past the
