@@ -457,17 +457,37 @@ def test_guard_bands():
     assert_tol(f64(ybig2[1:T + 1]), y_ref, "guarded fused")
 
 
-def test_graph_capture_equals_eager():
-    """A whole step (addressing + fused apply) recorded in a graph, replayed
-    with new token_slot contents, matches eager execution bit for bit."""
+GRAPH_CASES = {
+    "decode": (2, {}),
+    # a large batch: SGMV tiles for every segment, K parts in the workspace
+    "large": (5, dict(T=2048, in_features=2048, slots=64, out_slices=(512, 128, 128))),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GRAPH_CASES))
+@pytest.mark.parametrize("fused", [True, False])
+def test_graph_capture_equals_eager(case, fused):
+    """A whole step (addressing + apply, or addressing + shrink + expand)
+    recorded in a graph, replayed with new token_slot contents, matches eager
+    execution bit for bit on every replay."""
+    log(f"graph capture {case} fused={fused}")
     t = torch()
-    wl = W.make_config(2, 0)
+    k, over = GRAPH_CASES[case]
+    wl = W.make_config(k, 0, **over)
     tg = wl.targets[0]
     g = GpuTarget(wl, tg)
     ts = g.token_slot.clone()
     y = g.y0.clone()
     addr = L.build_addressing(ts, wl.slots)
-    L.apply_linear_(g.x, y, g.a, g.b, addr, g.ranks, g.scal, tg.out_slices)   # warm-up
+
+    def apply(a, yy):
+        if fused:
+            L.apply_linear_(g.x, yy, g.a, g.b, a, g.ranks, g.scal, tg.out_slices)
+        else:
+            h = L.shrink(g.x, g.a, a, g.ranks, tg.num_slices)
+            L.expand_(h, g.b, a, g.ranks, g.scal, yy, tg.out_slices)
+
+    apply(addr, y)   # warm-up
     t.cuda.synchronize()
     graph = t.cuda.CUDAGraph()
     s = t.cuda.Stream()
@@ -475,7 +495,7 @@ def test_graph_capture_equals_eager():
         y.copy_(g.y0)
         with t.cuda.graph(graph, stream=s):
             L.build_addressing(ts, wl.slots, out=addr)
-            L.apply_linear_(g.x, y, g.a, g.b, addr, g.ranks, g.scal, tg.out_slices)
+            apply(addr, y)
     t.cuda.synchronize()
     rng = np.random.default_rng(9)
     for rep in range(4):
@@ -489,7 +509,7 @@ def test_graph_capture_equals_eager():
         # eager on fresh buffers
         y_e = g.y0.clone()
         a_e = L.build_addressing(t.from_numpy(new).to("cuda:0"), wl.slots)
-        L.apply_linear_(g.x, y_e, g.a, g.b, a_e, g.ranks, g.scal, tg.out_slices)
+        apply(a_e, y_e)
         t.cuda.synchronize()
         assert t.equal(addr.token_order, a_e.token_order)
         assert t.equal(addr.slot_indptr, a_e.slot_indptr)
