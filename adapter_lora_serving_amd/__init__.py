@@ -41,7 +41,8 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_version": (ctypes.c_char_p, []),
-    "lora_build_addressing": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "lora_build_addressing": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _SZ, _P]),
+    "lora_build_addressing_workspace_bytes": (_SZ, [_I64, _I32]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P,
                                    _P, _P, _P, _SZ, _P]),
     "lora_shrink_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
@@ -141,8 +142,12 @@ def build_addressing(token_slot, slots: int, out: Optional[Addressing] = None) -
         out = Addressing(torch.empty(T, dtype=torch.int32, device=dev),
                          torch.empty(slots + 1, dtype=torch.int32, device=dev))
     _dev(token_slot, *out)
+    # the two-pass sort of a large batch takes a workspace (torch's caching
+    # allocator; no initialisation needed)
+    nws = int(lib().lora_build_addressing_workspace_bytes(T, slots))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
     st = lib().lora_build_addressing(_ptr(token_slot), T, slots, _ptr(out.token_order),
-                                     _ptr(out.slot_indptr), _stream(dev))
+                                     _ptr(out.slot_indptr), _ptr(ws), nws, _stream(dev))
     _check(st, "lora_build_addressing")
     return out
 

@@ -197,6 +197,81 @@ __global__ __launch_bounds__(64) void k_build_addressing_wave(
   }
 }
 
+// Large batches with a workspace: two passes over blocks of 1024 tokens
+// (16 waves x one group each). Pass 1 writes each block's per-key counts to
+// the workspace; pass 2 gives every block the count of each key in the
+// blocks before it and the key totals (so the segment starts), and scatters
+// its tokens: position = segment start + count in earlier blocks + count in
+// earlier waves of the block + rank in the group. Stable, like the
+// one-workgroup kernel, and spread over ceil(T/1024) workgroups.
+constexpr int kBlockTok = 16 * kWave;
+
+__global__ __launch_bounds__(1024) void k_addr_block_hist(const int32_t* __restrict__ token_slot,
+                                                          int T, int slots,
+                                                          int32_t* __restrict__ ws) {
+  extern __shared__ int smem[];   // [16][S1] per-wave counts
+  const int S1 = slots + 1;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int nbits = 32 - __clz(slots);
+  for (int i = tid; i < 16 * S1; i += kBlockTok) smem[i] = 0;
+  const int t = blockIdx.x * kBlockTok + tid;
+  const GroupMatch g = match_group(token_slot, t, t < T, slots, nbits);
+  __syncthreads();
+  if (g.leader) smem[w * S1 + g.key] += g.count;   // distinct keys: no collision
+  __syncthreads();
+  for (int k = tid; k < S1; k += kBlockTok) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c += smem[q * S1 + k];
+    ws[(int64_t)blockIdx.x * S1 + k] = c;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_addr_block_scatter(
+    const int32_t* __restrict__ token_slot, int T, int slots, const int32_t* __restrict__ ws,
+    int nb, int32_t* __restrict__ token_order, int32_t* __restrict__ slot_indptr) {
+  extern __shared__ int smem[];
+  const int S1 = slots + 1;
+  int* cnt = smem;              // [16][S1]: per-wave counts, then offsets in the block
+  int* base = cnt + 16 * S1;    // [S1]: segment start + count in earlier blocks
+  int* scratch = base + S1;     // [20]
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
+  const int nbits = 32 - __clz(slots);
+  const int b = blockIdx.x;
+  for (int i = tid; i < 16 * S1; i += kBlockTok) cnt[i] = 0;
+  const int t = b * kBlockTok + tid;
+  const GroupMatch g = match_group(token_slot, t, t < T, slots, nbits);
+  __syncthreads();
+  if (g.leader) cnt[w * S1 + g.key] += g.count;
+  __syncthreads();
+  // key k = tid (S1 <= 1024): total over all blocks, count in earlier ones,
+  // and the offsets of the block's waves
+  int tot = 0, pre = 0;
+  if (tid < S1) {
+    for (int bb = 0; bb < nb; ++bb) {
+      const int c = ws[(int64_t)bb * S1 + tid];
+      tot += c;
+      pre += bb < b ? c : 0;
+    }
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int c = cnt[q * S1 + tid];
+      cnt[q * S1 + tid] = run;
+      run += c;
+    }
+  }
+  const int start = block_exclusive_scan(tid < S1 ? tot : 0, scratch, nullptr);
+  if (tid < S1) {
+    base[tid] = start + pre;
+    if (b == 0) slot_indptr[tid] = start;
+  }
+  __syncthreads();
+  if (t < T) token_order[base[g.key] + cnt[w * S1 + g.key] + g.rank] = t;
+}
+
 int addressing_waves(int64_t T, int slots) {
   int nw = (int)((T + kWave - 1) / kWave);
   if (nw < 1) nw = 1;
@@ -211,9 +286,38 @@ size_t addressing_lds_bytes(int nw, int slots) {
   return (size_t)((nw + 1) * (slots + 1) + 20) * sizeof(int);
 }
 
+size_t addressing_workspace_bytes(int64_t T, int slots) {
+  // the two-pass path: batches past one block, keys within one per thread
+  if (T <= kBlockTok || slots + 1 > kBlockTok) return 0;
+  const int64_t nb = (T + kBlockTok - 1) / kBlockTok;
+  return (size_t)nb * (slots + 1) * sizeof(int32_t);
+}
+
 hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
-                                   int32_t* token_order, int32_t* slot_indptr,
-                                   hipStream_t stream) {
+                                   int32_t* token_order, int32_t* slot_indptr, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  const size_t need = addressing_workspace_bytes(T, slots);
+  if (ws && need > 0 && ws_bytes >= need) {
+    const int nb = (T + kBlockTok - 1) / kBlockTok;
+    const int S1 = slots + 1;
+    const size_t lds1 = (size_t)16 * S1 * sizeof(int);
+    const size_t lds2 = ((size_t)17 * S1 + 20) * sizeof(int);
+    if (lds2 > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_addr_block_hist,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)k_addr_block_scatter,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_addr_block_hist, dim3(nb), dim3(kBlockTok), lds1, stream, token_slot, T,
+                       slots, (int32_t*)ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_addr_block_scatter, dim3(nb), dim3(kBlockTok), lds2, stream, token_slot,
+                       T, slots, (const int32_t*)ws, nb, token_order, slot_indptr);
+    return hipGetLastError();
+  }
   if (slots + 1 <= kWave && T <= 16 * kWave) {
     const int groups = (T + kWave - 1) / kWave;
 #define W(GV)                                                                                    \

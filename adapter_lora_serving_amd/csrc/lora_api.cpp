@@ -86,14 +86,26 @@ const char* lora_status_string(int status) {
 
 const char* lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
 
+size_t lora_build_addressing_workspace_bytes(int64_t T, int32_t slots) {
+  if (T < 0 || T > kMaxI32 || slots < 1 || slots > 8192) return 0;
+  return lora::addressing_workspace_bytes(T, slots);
+}
+
 lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t slots,
-                                  int32_t* token_order, int32_t* slot_indptr, void* stream) {
+                                  int32_t* token_order, int32_t* slot_indptr, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (T < 0 || T > kMaxI32) return LORA_ERR_INVALID_ARG;
   if (slots < 1 || slots > 8192) return LORA_ERR_UNSUPPORTED;
   if (!slot_indptr) return LORA_ERR_INVALID_ARG;
   if (T > 0 && (!token_slot || !token_order)) return LORA_ERR_INVALID_ARG;
+  if (workspace) {
+    if (workspace_bytes < lora_build_addressing_workspace_bytes(T, slots))
+      return LORA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LORA_ERR_ALIGNMENT;
+  }
   return hip_status(lora::launch_build_addressing(token_slot, (int)T, slots, token_order,
-                                                  slot_indptr, (hipStream_t)stream));
+                                                  slot_indptr, workspace, workspace_bytes,
+                                                  (hipStream_t)stream));
 }
 
 size_t lora_shrink_workspace_bytes(int64_t T, int64_t in_features, int32_t num_slices,

@@ -30,9 +30,11 @@ struct ChunkTable {
   int c1[kMaxChunks];
 };
 
+// Workspace bytes for the two-pass path of the addressing (0: one pass).
+size_t addressing_workspace_bytes(int64_t T, int slots);
 hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
-                                   int32_t* token_order, int32_t* slot_indptr,
-                                   hipStream_t stream);
+                                   int32_t* token_order, int32_t* slot_indptr, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_gather_shrink(int dtype, const int32_t* ids, int T, int64_t vocab,
                                 const void* a, int slots, int R, const int32_t* token_order,

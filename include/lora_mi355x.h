@@ -97,10 +97,22 @@ const char* lora_version(void);
  * the number of live tokens. Deterministic and bit-exact.
  * token_slot [T] (read), token_order [T], slot_indptr [slots+1] (written).
  * T == 0 writes slot_indptr = 0 and nothing else.
+ * workspace (device, optional): with at least
+ * lora_build_addressing_workspace_bytes(T, slots) bytes (nonzero only for a
+ * batch of more than 1024 tokens over at most 1023 slots), 16-byte aligned,
+ * the batch is sorted by one workgroup per 1024 tokens in two passes; NULL
+ * (with workspace_bytes 0) sorts it in one workgroup. The result is the
+ * same. Contents need no initialisation; calls sharing one workspace must
+ * not overlap in time. A non-NULL workspace that is too small is
+ * LORA_ERR_WORKSPACE.
  */
 lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t slots,
-                                  int32_t* token_order, int32_t* slot_indptr,
-                                  void* stream);
+                                  int32_t* token_order, int32_t* slot_indptr, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_build_addressing can use (0: it would not use one,
+ * or bad input, which the call itself reports). */
+size_t lora_build_addressing_workspace_bytes(int64_t T, int32_t slots);
 
 /*
  * lora_shrink: h[t, i*R + j] = x[t] . a[slot(t), i*R + j] for j < rank(slot(t)).

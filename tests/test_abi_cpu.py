@@ -136,10 +136,18 @@ def test_apply_linear_validation_and_workspace(lib):
 
 def test_addressing_validation(lib):
     f = lib.lora_build_addressing
-    assert f(A16, -1, 4, A16, A16, None) == INVALID
-    assert f(A16, 4, 0, A16, A16, None) == UNSUPPORTED
-    assert f(A16, 4, 4, A16, None, None) == INVALID
-    assert f(None, 4, 4, A16, A16, None) == INVALID
+    assert f(A16, -1, 4, A16, A16, None, 0, None) == INVALID
+    assert f(A16, 4, 0, A16, A16, None, 0, None) == UNSUPPORTED
+    assert f(A16, 4, 4, A16, None, None, 0, None) == INVALID
+    assert f(None, 4, 4, A16, A16, None, 0, None) == INVALID
+    # the two-pass workspace: one count per (1024-token block, key)
+    need = lib.lora_build_addressing_workspace_bytes(8192, 16)
+    assert need == 8 * 17 * 4
+    assert lib.lora_build_addressing_workspace_bytes(1024, 16) == 0     # one block
+    assert lib.lora_build_addressing_workspace_bytes(8192, 1024) == 0   # keys > 1024
+    assert lib.lora_build_addressing_workspace_bytes(-1, 16) == 0
+    assert f(A16, 8192, 16, A16, A16, A16, need - 1, None) == WORKSPACE
+    assert f(A16, 8192, 16, A16, A16, A16 + 8, need, None) == ALIGN
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -72,6 +72,28 @@ def test_addressing_edges(T, slots, dead):
     _addr_case(ts, slots)
 
 
+@pytest.mark.parametrize("T,slots", [(8192, 16), (70000, 64), (3000, 900)])
+def test_addressing_one_workgroup(T, slots):
+    """Without a workspace a large batch is sorted by the one-workgroup
+    kernel; the same result as the oracle (and so as the two-pass sort the
+    binding runs)."""
+    log(f"addressing one workgroup T={T} slots={slots}")
+    t = torch()
+    rng = np.random.default_rng(T ^ slots)
+    ts = rng.integers(-1, slots, size=T).astype(np.int32)
+    tsd = t.from_numpy(ts).to("cuda:0")
+    order = t.empty(T, dtype=t.int32, device="cuda:0")
+    indptr = t.empty(slots + 1, dtype=t.int32, device="cuda:0")
+    st = L.lib().lora_build_addressing(tsd.data_ptr(), T, slots, order.data_ptr(),
+                                       indptr.data_ptr(), None, 0,
+                                       t.cuda.current_stream().cuda_stream)
+    assert st == 0
+    t.cuda.synchronize()
+    o_ref, i_ref = O.build_addressing(ts, slots)
+    assert np.array_equal(order.cpu().numpy(), o_ref)
+    assert np.array_equal(indptr.cpu().numpy(), i_ref)
+
+
 # ---------------------------------------------------------------------------
 # gather_shrink (+ expand): config 4
 # ---------------------------------------------------------------------------
