@@ -9,13 +9,15 @@
 // scalings[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T); the slice
 // layout follows mstar.model.components.linear, FusedColumnLinear.
 //
-// Shrink item: (slot, block of 128 tokens of its segment, slice, K part).
-//   Eight waves; wave w owns token tile w against every rank tile. Its x
-//   rows go straight from HBM into registers a few 64-element chunks ahead;
-//   A's chunk is shared through a double-buffered LDS tile. Rows of A at or
-//   past the rank lie outside the A resource and read as zeros without a
-//   memory access. With several K parts each item writes a partial h and a
-//   second kernel sums the parts.
+// Shrink item: (slot, block of 128 tokens of its segment, slice group, K
+//   part). Eight waves; wave w owns token tile w against every rank tile.
+//   Its x rows go straight from HBM into registers a few 64-element chunks
+//   ahead; A's chunk is shared through a double-buffered LDS tile. A slot
+//   whose rank needs fewer rank tiles than the kernel holds takes several
+//   slices in one item (their tiles side by side), so its x block is read
+//   once for all of them. Rows of A at or past the rank read as zeros
+//   without a memory access. With several K parts each item writes a
+//   partial h and a second kernel sums the parts.
 // Expand item: (slot, block of 64 tokens, 256 output columns of one slice).
 //   The block's h rows are scaled and split into bf16 hi + lo in LDS; every
 //   wave prefetches its 4 column tiles of B and y in one round trip, then
@@ -29,6 +31,8 @@
 // that XCD's L2. A shrink item's K parts are innermost for the same reason.
 #include "lora_common.h"
 #include "lora_kernels.h"
+
+#include <algorithm>
 
 namespace lora {
 
@@ -51,24 +55,36 @@ __device__ __forceinline__ int block_item(int n) {
 // ---------------------------------------------------------------------------
 // shrink
 // ---------------------------------------------------------------------------
-// Item: (slot, block of 128 tokens, slice, K part). Eight waves, wave w owns
-// token tile w (16 tokens) against every rank tile, so its x rows are its own
-// (read into registers D chunks ahead) and only A is shared: A's
+// Item: (slot, block of 128 tokens, slice group, K part). Eight waves, wave w
+// owns token tile w (16 tokens) against every rank tile, so its x rows are
+// its own (read into registers D chunks ahead) and only A is shared: A's
 // chunk [RP x 64] goes through a register ring D chunks ahead into a
 // double-buffered LDS tile. A is thus re-read from L2 once per 128 tokens.
+// A slot of rank r uses ntr = ceil(r / 16) rank tiles per slice; a group
+// packs g = min(S, RT / ntr, gmax) slices, slice j of the group on tiles
+// [j * ntr, (j + 1) * ntr). gmax keeps a group's A rows below 2 GiB.
 // With kparts > 1 each item writes its partial h to its own buffer
-// (hout + kp * part_stride); k_sum_parts adds them in kp order.
+// (hout + kp * part_stride); k_sum_parts adds them in kp order. Every item
+// writes all R columns of each of its slices (zeros from ntr * 16 on).
 constexpr int kBMs = 128;
 constexpr int kD = 4;
 
+// Slices per item for a slot of rank r (r > 0) in a kernel of RT rank tiles.
+__device__ __forceinline__ int shrink_group(int r, int RT, int S, int gmax) {
+  const int ntr = (r + 15) / 16;
+  return max(1, min(min(S, RT / ntr), gmax));
+}
+
 template <int RT>
 // Six waves per SIMD (three workgroups per CU) keep a prefill batch's items
-// resident in one round, so no item starts after the first round ends.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k_sgmv_shrink(
+// resident in one round, so no item starts after the first round ends; at 16
+// rank tiles the LDS allows two workgroups per CU, so four waves per SIMD
+// (128 VGPRs) are enough and keep the accumulators in registers.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 4 : 6))) void k_sgmv_shrink(
     const void* __restrict__ x_, int T, int in, const void* __restrict__ a_, int slots, int S,
     int R, const int32_t* __restrict__ order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, float* __restrict__ hout, int kparts,
-    int64_t part_stride, int min_len) {
+    int64_t part_stride, int min_len, int gmax) {
   constexpr int RP = RT * 16;
   constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
   constexpr int D = RT >= 8 ? 2 : RT >= 4 ? 3 : kD;   // chunks in flight (register budget)
@@ -92,7 +108,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
         v[2] = clamp_rank(ranks[ss], R);
       },
       [&](const int* v) {
-        return (v[1] > min_len && v[2] > 0) ? S * kparts * ((v[1] + kBMs - 1) / kBMs) : 0;
+        if (v[1] <= min_len || v[2] <= 0) return 0;
+        const int g = shrink_group(v[2], RT, S, gmax);
+        return (S + g - 1) / g * kparts * ((v[1] + kBMs - 1) / kBMs);
       },
       scratch);
   if (it.slot < 0) return;
@@ -104,15 +122,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int kp = it.local % kparts;
   const int rest = it.local / kparts;
   const int mb = rest % nmb;
-  const int i = rest / nmb;
+  const int ntr = (r + 15) / 16;   // rank tiles of one slice
+  const int g = shrink_group(r, RT, S, gmax);
+  const int i0 = (rest / nmb) * g;  // first slice of the group
+  const int gsz = min(g, S - i0);   // slices in the group
+  const int live = gsz * ntr;       // rank tiles holding rows below r
   const int ntok = min(kBMs, n - mb * kBMs);
   // the token ids are the oldest loads in flight; the first A chunks (which
   // do not depend on them) are issued next, then the ids are waited for
   const int tv = token_at(order, seg0 + mb * kBMs + min(tid, ntok - 1), T);
 
   const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
-  const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S * R + (int64_t)i * R) * in * 2,
-                               (uint32_t)r * (uint32_t)in * 2u);
+  // the group's A rows: slices i0 .. i0 + gsz - 1 of the slot
+  const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S + i0) * R * in * 2,
+                               (uint32_t)gsz * (uint32_t)R * (uint32_t)in * 2u);
   const uint32_t rowG = (uint32_t)in * 2u;
   const int nchT = (in + kKC - 1) / kKC;
   const int cbeg = (int)((int64_t)nchT * kp / kparts);
@@ -123,6 +146,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
   const int kg = lane >> 4;
   const int arow = tid >> 3;        // 0..63 (+64 per extra piece)
   const int apc = tid & 7;
+  // LDS tile row v holds row v % (16 ntr) of slice v / (16 ntr) of the group
+  uint32_t abase[AL];
+#pragma unroll
+  for (int q = 0; q < AL; ++q) {
+    const int v = arow + 64 * q;
+    const int j = v / (16 * ntr);
+    const int rr = v - j * 16 * ntr;
+    abase[q] = (v < RP && j < gsz && rr < r) ? (uint32_t)(j * R + rr) * rowG : kOOB;
+  }
 
   u32x4 xr[D][2];
   u32x4 ar[D][AL];
@@ -131,10 +163,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
 #pragma unroll
     for (int q = 0; q < AL; ++q) {
-      const int row = arow + 64 * q;
       const uint32_t e = (uint32_t)((cbeg + c) * kKC + apc * 8);
-      ar[slot][q] = bload16(a_r, (cv && row < RP && e < (uint32_t)in)
-                                     ? (uint32_t)row * rowG + kb + apc * 16u
+      ar[slot][q] = bload16(a_r, (cv && abase[q] != kOOB && e < (uint32_t)in)
+                                     ? abase[q] + kb + apc * 16u
                                      : kOOB);
     }
   };
@@ -172,7 +203,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     }
   };
 
-  const int ntr = (r + 15) / 16;   // rank tiles holding rows below r
   f32x4 acc[RT];
 #pragma unroll
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -203,10 +233,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
             xa = __builtin_bit_cast(bf16x8, xr[d][ks]);
 #pragma unroll
           for (int nt = 0; nt < RT; ++nt) {
-            if (nt >= ntr) break;   // rank tiles past r hold only zeros
-            const bf16x8 av = __builtin_bit_cast(
-                bf16x8, *(const u32x4*)(ab + (nt * 16 + m) * kRowB + (ks * 32 + kg * 8) * 2));
-            acc[nt] = mfma_k32(xa, av, acc[nt]);
+            // tiles past the group's rows hold only zeros (16 tiles take a
+            // guard instead of an early exit, so that the loop unrolls)
+            if (RT < 16 && nt >= live) break;
+            if (nt < live) {
+              const bf16x8 av = __builtin_bit_cast(
+                  bf16x8, *(const u32x4*)(ab + (nt * 16 + m) * kRowB + (ks * 32 + kg * 8) * 2));
+              acc[nt] = mfma_k32(xa, av, acc[nt]);
+            }
           }
         }
         issue_a(d, c + D);
@@ -216,18 +250,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) void k
     }
   }
 
-  // lane (m, kg) holds h[token w*16 + 4kg + ii][rank nt*16 + m]
+  // lane (m, kg) holds h[token w*16 + 4kg + ii][slice i0 + nt / ntr, rank
+  // (nt % ntr) * 16 + m]
   const int SR = S * R;
   float* hp = hout + (int64_t)kp * part_stride;
+  if constexpr (RT < 16) {
 #pragma unroll
-  for (int nt = 0; nt < RT; ++nt) {
-    const int j = nt * 16 + m;
-    if (j < R) {
+    for (int nt = 0; nt < RT; ++nt) {
+      if (nt >= live) break;
+      const int j = nt / ntr;
+      const int rr = (nt - j * ntr) * 16 + m;
+      if (rr < R) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int tt = tok[w * 16 + 4 * kg + ii];
-        if (tt >= 0) hp[(int64_t)tt * SR + i * R + j] = acc[nt][ii];
+        for (int ii = 0; ii < 4; ++ii) {
+          const int tt = tok[w * 16 + 4 * kg + ii];
+          if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + rr] = acc[nt][ii];
+        }
       }
+    }
+  } else {   // 16 tiles: no early exit, so that the loop unrolls
+    int j = 0, rt = 0;   // slice in the group and rank tile of tile nt
+#pragma unroll
+    for (int nt = 0; nt < RT; ++nt) {
+      const int rr = rt * 16 + m;
+      if (nt < live && rr < R) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int tt = tok[w * 16 + 4 * kg + ii];
+          if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + rr] = acc[nt][ii];
+        }
+      }
+      if (++rt == ntr) { rt = 0; ++j; }
+    }
+  }
+  // columns [16 ntr, R) of each slice: zeros (rank rows past r)
+  const int zc = R - 16 * ntr;
+  if (zc > 0) {
+    for (int idx = lane; idx < 16 * gsz * zc; idx += kWave) {
+      const int q = idx / (gsz * zc);
+      const int rem = idx - q * gsz * zc;
+      const int j = rem / zc;
+      const int tt = tok[w * 16 + q];
+      if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + 16 * ntr + (rem - j * zc)] = 0.f;
     }
   }
 }
@@ -435,8 +499,10 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
     return __builtin_bit_cast(s16x4, p ? u32x2{v.z, v.w} : u32x2{v.x, v.y});
   };
   float* sw = stage[w];
+  const int mtl = (ntok + 15) / 16;   // token tiles holding tokens
 #pragma unroll
   for (int q = 0; q < MT; ++q) {
+    if (q >= mtl) break;
     u32x4 hq[KS], lq[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -522,9 +588,13 @@ hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int s
   const int64_t grid = 8 * ((items + 7) / 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   float* dst = kparts > 1 ? parts : h;
+  // slices per item at most: their A rows must stay below 2 GiB
+  const int64_t slice_bytes = (int64_t)R * in * 2;
+  const int gmax = (int)std::max<int64_t>(1, std::min<int64_t>(S, (((int64_t)1 << 31) - 1) /
+                                                                       slice_bytes));
 #define L(RTV)                                                                                 \
   hipLaunchKernelGGL(k_sgmv_shrink<RTV>, dim3((unsigned)grid), dim3(512), 0, stream, x, T, in, \
-                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len)
+                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len, gmax)
   switch (rt_of(R)) {
     case 1: L(1); break;
     case 2: L(2); break;

@@ -354,6 +354,10 @@ EDGE = {
     # leaves most segments a few tokens long
     "large_skewed": dict(T=2048, in_f=1024, out_slices=(512, 128, 128), R=128, slots=96,
                          ranks=[128, 64, 32, 16, 8, 0] * 16, skew=1.2, dead=0.02),
+    # the largest rank on the SGMV tiles (16 rank tiles), with slices grouped
+    # per item for the small ranks
+    "large_rank256": dict(T=1100, in_f=648, out_slices=(256, 96, 32), R=256, slots=6,
+                          ranks=[256, 200, 17, 0, 128, 48], dead=0.02),
 }
 
 
