@@ -236,6 +236,82 @@ __device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, InfoFn
   return r;
 }
 
+// Slot scan kept in registers for a workgroup that locates several items
+// (a grid-stride loop): scan_slots loads each slot's values once and forms
+// the block-wide exclusive prefix of the per-slot item counts; pick_item then
+// finds any item's slot without another scan. Same contract as
+// locate_picked: info(s, v) loads (segment begin, length, rank) and
+// count_of(v) gives the slot's items.
+struct SlotScan {
+  int s0, s1;    // this thread's slots [s0, s1)
+  int excl;      // items before slot s0
+  int local;     // items of this thread's slots
+  int first;     // items of slot s0
+  int v0[3];     // values of slot s0
+  int total;     // items over all slots
+};
+
+template <typename InfoFn, typename CountFn>
+__device__ __forceinline__ SlotScan scan_slots(int slots, InfoFn info, CountFn count_of,
+                                               int* scratch /* >= 24 ints LDS */) {
+  SlotScan sc;
+  const int nthreads = blockDim.x;
+  const int chunk = (slots + nthreads - 1) / nthreads;
+  sc.s0 = threadIdx.x * chunk;
+  sc.s1 = min(slots, sc.s0 + chunk);
+  sc.v0[0] = sc.v0[1] = sc.v0[2] = 0;
+  sc.local = 0;
+  sc.first = 0;
+  for (int s = sc.s0; s < sc.s1; ++s) {
+    int v[3];
+    info(s, v);
+    const int c = count_of(v);
+    if (s == sc.s0) {
+      sc.first = c;
+      sc.v0[0] = v[0]; sc.v0[1] = v[1]; sc.v0[2] = v[2];
+    }
+    sc.local += c;
+  }
+  sc.excl = block_exclusive_scan(sc.local, scratch, &sc.total);
+  sc.total = __builtin_amdgcn_readfirstlane(sc.total);
+  return sc;
+}
+
+// Slot of `item` (< sc.total): fills it (slot, local, total) and v (the
+// slot's values). Every thread of the block must call it; the caller keeps
+// a __syncthreads() between one call's return and the next call.
+template <typename InfoFn, typename CountFn>
+__device__ __forceinline__ void pick_item(const SlotScan& sc, int item, InfoFn info,
+                                          CountFn count_of, int* scratch, SlotItem& it,
+                                          int* v) {
+  if (threadIdx.x == 0) scratch[18] = -1;
+  __syncthreads();
+  if (item >= sc.excl && item < sc.excl + sc.local) {
+    int run = sc.excl;
+    for (int s = sc.s0; s < sc.s1; ++s) {
+      int u[3] = {sc.v0[0], sc.v0[1], sc.v0[2]};
+      if (s != sc.s0) info(s, u);
+      const int c = s == sc.s0 ? sc.first : count_of(u);
+      if (item < run + c) {
+        scratch[18] = s;
+        scratch[19] = item - run;
+        scratch[20] = u[0];
+        scratch[21] = u[1];
+        scratch[22] = u[2];
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  // uniform values: held in scalar registers
+  it = SlotItem{__builtin_amdgcn_readfirstlane(scratch[18]),
+                __builtin_amdgcn_readfirstlane(scratch[19]), sc.total};
+  v[0] = __builtin_amdgcn_readfirstlane(scratch[20]);
+  v[1] = __builtin_amdgcn_readfirstlane(scratch[21]);
+  v[2] = __builtin_amdgcn_readfirstlane(scratch[22]);
+}
+
 // Raw buffer access. A resource covers [base, base + bytes); a load at an
 // offset outside it returns zero without touching memory and a store there is
 // dropped, so predicated accesses need no branches (kOOB is such an offset

@@ -335,7 +335,14 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
 // it is staged through a per-wave LDS tile so that y is read and written
 // row-major: one instruction covers 8 token rows x 128 contiguous bytes,
 // full cache lines, so HBM never sees partial-line writes.
-template <int RT>
+// PERSIST: a workgroup runs items blockIdx.x, blockIdx.x + gridDim.x, ...
+// (the grid is about one resident round, a multiple of 8, so an item's XCD
+// is still item % 8). The slot scan is done once; while an item runs, the
+// next item's slot is picked and its token ids are loaded, so an item starts
+// with its B, h and y requests instead of two dependent round trips. That
+// pays where most items are short (many short segments); otherwise one item
+// per workgroup lets the dispatcher balance the load.
+template <int RT, bool PERSIST>
 __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int T, SliceTable st,
                                                      const float* __restrict__ h,
                                                      const void* __restrict__ b_, int slots,
@@ -367,191 +374,239 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   int nck = 0;
   for (int i = 0; i < S; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
   const int nck8 = (nck + 7) & ~7;   // chunk slots per token block (padding items idle)
-  const SlotItem it = locate_picked(
-      [&](int total) { return block_item(total); }, slots,
-      [&](int ss, int* v) {
-        segment_of(indptr, ss, T, v[0], v[1]);
-        v[2] = clamp_rank(ranks[ss], R);
-      },
-      [&](const int* v) {
-        return (v[1] > min_len && v[2] > 0) ? nck8 * ((v[1] + kBMe - 1) / kBMe) : 0;
-      },
-      scratch);
-  if (it.slot < 0) return;
-  const int s = it.slot;
-  const int seg0 = scratch[20];
-  const int n = scratch[21];
-  const int r = scratch[22];
-  const int mb = it.local / nck8;
-  int ck = it.local % nck8;
-  if (ck >= nck) return;
-  int i = 0;
-  for (; i < S; ++i) {
-    const int c = (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
-    if (ck < c) break;
-    ck -= c;
-  }
-  const int lo = st.off[i] + ck * kCC;
-  const int hi = min(lo + kCC, st.off[i + 1]);
-  const int ntok = min(kBMe, n - mb * kBMe);
-  // the token ids are the oldest loads in flight; the B tiles (which do not
-  // depend on them) are issued next, then the ids are waited for
-  const int tv = token_at(order, seg0 + mb * kBMe + min(tid, ntok - 1), T);
-
-  const int m = lane & 15;
-  const int kg = lane >> 4;
-  const rsrc_t y_r = make_rsrc(y_, (uint32_t)T * (uint32_t)out * 2u);
-  const rsrc_t b_r = make_rsrc((const char*)b_ + (int64_t)s * out * R * 2,
-                               (uint32_t)out * (uint32_t)R * 2u);
-  const int ntiles = (hi - lo) >> 4;
-  const int cw = lo + w * 64;         // this wave's first column
-  const int ntr = (r + KW - 1) / KW;  // rank steps holding ranks below r
-  // lane (m, kg) holds B[column][ranks kk, kk + KW/4) of each of its tiles
-  u32x4 bq[TPW][KS];
-#pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = w * TPW + u;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kk = ks * KW + kg * (KW / 4);
-      const uint32_t off = (tile < ntiles && kk < r)
-                               ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
-                               : kOOB;
-      if constexpr (K32) {
-        bq[u][ks] = bload16(b_r, off);
-      } else {
-        const u32x2 v = bload8(b_r, off);
-        bq[u][ks] = u32x4{v.x, v.y, 0u, 0u};
-      }
-    }
-  }
-  if (tid < kBMe) tok[tid] = tid < ntok ? tv : -1;
-  __syncthreads();
-
-  // row-major y access: lane -> rows (lane >> 3) and 8 + (lane >> 3) of a
-  // token tile, 16-byte piece (lane & 7) of the wave's 128-byte column span
-  const int prow = lane >> 3;
-  const int ppc = lane & 7;
-  const bool pcol = (w * TPW + (ppc >> 1)) < ntiles;   // piece inside the chunk
-  u32x4 yv[MT][2];
-#pragma unroll
-  for (int q = 0; q < MT; ++q)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int t = tok[q * 16 + prow + 8 * hh];
-      yv[q][hh] = bload16(y_r, (pcol && t >= 0)
-                                   ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
-                                   : kOOB);
-    }
-
-  // h rows of the block, 4 ranks per load (ranks at or past r are set to
-  // zero; they are the block's own h columns, not adapter weights), scaled
-  // and split hi + lo; all of a thread's loads are issued before any is used
-  const float scale = scalings[s];
-  const int SR = S * R;
-  constexpr int RQ = RP / 4;                    // 16-byte pieces per h row
-  constexpr int HQ = (kBMe * RQ + 255) / 256;   // pieces per thread
-  const rsrc_t h_r = make_rsrc(h, (uint32_t)T * (uint32_t)SR * 4u);
-  u32x4 hv[HQ];
-#pragma unroll
-  for (int k = 0; k < HQ; ++k) {
-    const int idx = tid + 256 * k;
-    const int q = idx / RQ;
-    const int j = (idx - q * RQ) * 4;
-    const int t = q < kBMe ? tok[q] : -1;
-    hv[k] = bload16(h_r, (t >= 0 && j < r) ? ((uint32_t)t * (uint32_t)SR + i * R + j) * 4u
-                                           : kOOB);
-  }
-#pragma unroll
-  for (int k = 0; k < HQ; ++k) {
-    const int idx = tid + 256 * k;
-    const int q = idx / RQ;
-    const int j = (idx - q * RQ) * 4;
-    uint32_t hb[4], lb[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = (j + e < r) ? __uint_as_float(hv[k][e]) * scale : 0.f;
-      hb[e] = to_bf16_bits(v);
-      lb[e] = to_bf16_bits(v - __uint_as_float(hb[e] << 16));
-    }
-    if (q < kBMe) {
-      *(u32x2*)(hhi + q * RPS + j) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-      *(u32x2*)(hlo + q * RPS + j) = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
-    }
-  }
-  __syncthreads();
-
-  // ranks past r in a live step are never used
-#pragma unroll
-  for (int u = 0; u < TPW; ++u)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kk = ks * KW + kg * (KW / 4);
-#pragma unroll
-      for (int e = 0; e < (K32 ? 4 : 2); ++e) {
-        const uint32_t mlo = (kk + 2 * e < r) ? 0xffffu : 0u;
-        const uint32_t mhi = (kk + 2 * e + 1 < r) ? 0xffff0000u : 0u;
-        bq[u][ks][e] &= mlo | mhi;
-      }
-    }
-
-  auto half = [](u32x4 v, int p) {   // bf16 quadruple p (0 or 1) of a 16-byte piece
-    return __builtin_bit_cast(s16x4, p ? u32x2{v.z, v.w} : u32x2{v.x, v.y});
+  auto info = [&](int ss, int* v) {
+    segment_of(indptr, ss, T, v[0], v[1]);
+    v[2] = clamp_rank(ranks[ss], R);
   };
+  auto count_of = [&](const int* v) {
+    return (v[1] > min_len && v[2] > 0) ? nck8 * ((v[1] + kBMe - 1) / kBMe) : 0;
+  };
+  const SlotScan sc = scan_slots(slots, info, count_of, scratch);
+  int item = blockIdx.x;
+  if (item >= sc.total) return;
+  __syncthreads();   // the scan's scratch is reused by the picks
+
+  // the token id of thread tid (< 64) of an item: -1 past the item's tokens
+  auto token_of = [&](const SlotItem& it, const int* v) {
+    const int ntok = min(kBMe, v[1] - (it.local / nck8) * kBMe);
+    return tid < ntok ? token_at(order, v[0] + (it.local / nck8) * kBMe + tid, T) : -1;
+  };
+  SlotItem it;
+  int sv[3];
+  pick_item(sc, item, info, count_of, scratch, it, sv);
+  int tv = token_of(it, sv);
+
+  const rsrc_t y_r = make_rsrc(y_, (uint32_t)T * (uint32_t)out * 2u);
+  const int SR = S * R;
+  const rsrc_t h_r = make_rsrc(h, (uint32_t)T * (uint32_t)SR * 4u);
   float* sw = stage[w];
-  const int mtl = (ntok + 15) / 16;   // token tiles holding tokens
-#pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    if (q >= mtl) break;
-    u32x4 hq[KS], lq[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks >= ntr) break;
-      const int off = (q * 16 + m) * RPS + ks * KW + kg * (KW / 4);
-      if constexpr (K32) {
-        hq[ks] = *(const u32x4*)(hhi + off);
-        lq[ks] = *(const u32x4*)(hlo + off);
-      } else {
-        const u32x2 a = *(const u32x2*)(hhi + off);
-        const u32x2 c = *(const u32x2*)(hlo + off);
-        hq[ks] = u32x4{a.x, a.y, 0u, 0u};
-        lq[ks] = u32x4{c.x, c.y, 0u, 0u};
-      }
+
+  for (;;) {
+    // lane-derived offsets are formed again in every item: kept across the
+    // loop they would hold registers the item's loads need
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    const int lane_i = ltid & 63;
+    const int m = lane_i & 15;
+    const int kg = lane_i >> 4;
+    const int prow = lane_i >> 3;
+    const int ppc = lane_i & 7;
+    const int s = it.slot;
+    const int seg0 = sv[0];
+    const int n = sv[1];
+    const int r = sv[2];
+    const int mb = it.local / nck8;
+    int ck = it.local % nck8;
+    // the next item's slot (no memory access for up to 256 slots)
+    const int nitem = item + (int)gridDim.x;
+    SlotItem nit;
+    int nsv[3];
+    if (PERSIST && nitem < sc.total) {
+      __syncthreads();   // this item's pick was read by every thread
+      pick_item(sc, nitem, info, count_of, scratch, nit, nsv);
     }
+    if (ck < nck) {
+      int i = 0;
+      for (; i < S; ++i) {
+        const int c = (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
+        if (ck < c) break;
+        ck -= c;
+      }
+      const int lo = st.off[i] + ck * kCC;
+      const int hi = min(lo + kCC, st.off[i + 1]);
+      const int ntok = min(kBMe, n - mb * kBMe);
+      const rsrc_t b_r = make_rsrc((const char*)b_ + (int64_t)s * out * R * 2,
+                                   (uint32_t)out * (uint32_t)R * 2u);
+      const int ntiles = (hi - lo) >> 4;
+      const int cw = lo + w * 64;         // this wave's first column
+      const int ntr = (r + KW - 1) / KW;  // rank steps holding ranks below r
+      // lane (m, kg) holds B[column][ranks kk, kk + KW/4) of each of its tiles
+      u32x4 bq[TPW][KS];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < TPW; ++u) {
+        const int tile = w * TPW + u;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks >= ntr) break;
-#pragma unroll
-        for (int p = 0; p < (K32 ? 2 : 1); ++p) {
-          o = mfma_k16(half(bq[u][ks], p), half(hq[ks], p), o);
-          o = mfma_k16(half(bq[u][ks], p), half(lq[ks], p), o);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kk = ks * KW + kg * (KW / 4);
+          const uint32_t off = (tile < ntiles && kk < r)
+                                   ? ((uint32_t)(cw + u * 16 + m) * (uint32_t)R + kk) * 2u
+                                   : kOOB;
+          if constexpr (K32) {
+            bq[u][ks] = bload16(b_r, off);
+          } else {
+            const u32x2 v = bload8(b_r, off);
+            bq[u][ks] = u32x4{v.x, v.y, 0u, 0u};
+          }
         }
       }
-      // o[ii] = delta[token m][column 16u + 4kg + ii]
-      *(f32x4*)(sw + m * SRW + u * 16 + kg * 4) = o;
-    }
-    __builtin_amdgcn_wave_barrier();
+      if (tid < kBMe) tok[tid] = tv;
+      __syncthreads();
+
+      // row-major y access: lane -> rows (lane >> 3) and 8 + (lane >> 3) of a
+      // token tile, 16-byte piece (lane & 7) of the wave's 128-byte column span
+      const bool pcol = (w * TPW + (ppc >> 1)) < ntiles;   // piece inside the chunk
+      u32x4 yv[MT][2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = prow + 8 * hh;
-      const f32x4 d0 = *(const f32x4*)(sw + row * SRW + 8 * ppc);
-      const f32x4 d1 = *(const f32x4*)(sw + row * SRW + 8 * ppc + 4);
-      const u32x4 yy = yv[q][hh];
-      const int t = tok[q * 16 + row];
-      bstore16(y_r, (pcol && t >= 0) ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u : kOOB,
-               u32x4{pack_bf16x2(bf16lo(yy.x) + d0.x, bf16hi(yy.x) + d0.y),
-                     pack_bf16x2(bf16lo(yy.y) + d0.z, bf16hi(yy.y) + d0.w),
-                     pack_bf16x2(bf16lo(yy.z) + d1.x, bf16hi(yy.z) + d1.y),
-                     pack_bf16x2(bf16lo(yy.w) + d1.z, bf16hi(yy.w) + d1.w)});
+      for (int q = 0; q < MT; ++q)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int t = tok[q * 16 + prow + 8 * hh];
+          yv[q][hh] = bload16(y_r, (pcol && t >= 0)
+                                       ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
+                                       : kOOB);
+        }
+
+      // h rows of the block, 4 ranks per load (ranks at or past r are set to
+      // zero; they are the block's own h columns, not adapter weights), scaled
+      // and split hi + lo; all of a thread's loads are issued before any is used
+      const float scale = scalings[s];
+      constexpr int RQ = RP / 4;                    // 16-byte pieces per h row
+      constexpr int HQ = (kBMe * RQ + 255) / 256;   // pieces per thread
+      u32x4 hv[HQ];
+#pragma unroll
+      for (int k = 0; k < HQ; ++k) {
+        const int idx = ltid + 256 * k;
+        const int q = idx / RQ;
+        const int j = (idx - q * RQ) * 4;
+        const int t = q < kBMe ? tok[q] : -1;
+        hv[k] = bload16(h_r, (t >= 0 && j < r) ? ((uint32_t)t * (uint32_t)SR + i * R + j) * 4u
+                                               : kOOB);
+      }
+      // the next item's token ids: in flight while this item computes
+      if (PERSIST && nitem < sc.total) tv = token_of(nit, nsv);
+#pragma unroll
+      for (int k = 0; k < HQ; ++k) {
+        const int idx = ltid + 256 * k;
+        const int q = idx / RQ;
+        const int j = (idx - q * RQ) * 4;
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = (j + e < r) ? __uint_as_float(hv[k][e]) * scale : 0.f;
+          hb[e] = to_bf16_bits(v);
+          lb[e] = to_bf16_bits(v - __uint_as_float(hb[e] << 16));
+        }
+        if (q < kBMe) {
+          *(u32x2*)(hhi + q * RPS + j) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+          *(u32x2*)(hlo + q * RPS + j) = u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+        }
+      }
+      __syncthreads();
+
+      // ranks past r in a live step are never used
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int kk = ks * KW + kg * (KW / 4);
+#pragma unroll
+          for (int e = 0; e < (K32 ? 4 : 2); ++e) {
+            const uint32_t mlo = (kk + 2 * e < r) ? 0xffffu : 0u;
+            const uint32_t mhi = (kk + 2 * e + 1 < r) ? 0xffff0000u : 0u;
+            bq[u][ks][e] &= mlo | mhi;
+          }
+        }
+
+      auto half = [](u32x4 v, int p) {   // bf16 quadruple p (0 or 1) of a 16-byte piece
+        return __builtin_bit_cast(s16x4, p ? u32x2{v.z, v.w} : u32x2{v.x, v.y});
+      };
+      const int mtl = (ntok + 15) / 16;   // token tiles holding tokens
+#pragma unroll
+      for (int q = 0; q < MT; ++q) {
+        if (q >= mtl) break;
+        u32x4 hq[KS], lq[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks >= ntr) break;
+          const int off = (q * 16 + m) * RPS + ks * KW + kg * (KW / 4);
+          if constexpr (K32) {
+            hq[ks] = *(const u32x4*)(hhi + off);
+            lq[ks] = *(const u32x4*)(hlo + off);
+          } else {
+            const u32x2 a = *(const u32x2*)(hhi + off);
+            const u32x2 c = *(const u32x2*)(hlo + off);
+            hq[ks] = u32x4{a.x, a.y, 0u, 0u};
+            lq[ks] = u32x4{c.x, c.y, 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks >= ntr) break;
+#pragma unroll
+            for (int p = 0; p < (K32 ? 2 : 1); ++p) {
+              o = mfma_k16(half(bq[u][ks], p), half(hq[ks], p), o);
+              o = mfma_k16(half(bq[u][ks], p), half(lq[ks], p), o);
+            }
+          }
+          // o[ii] = delta[token m][column 16u + 4kg + ii]
+          *(f32x4*)(sw + m * SRW + u * 16 + kg * 4) = o;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = prow + 8 * hh;
+          const f32x4 d0 = *(const f32x4*)(sw + row * SRW + 8 * ppc);
+          const f32x4 d1 = *(const f32x4*)(sw + row * SRW + 8 * ppc + 4);
+          const u32x4 yy = yv[q][hh];
+          const int t = tok[q * 16 + row];
+          bstore16(y_r,
+                   (pcol && t >= 0) ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u : kOOB,
+                   u32x4{pack_bf16x2(bf16lo(yy.x) + d0.x, bf16hi(yy.x) + d0.y),
+                         pack_bf16x2(bf16lo(yy.y) + d0.z, bf16hi(yy.y) + d0.w),
+                         pack_bf16x2(bf16lo(yy.z) + d1.x, bf16hi(yy.z) + d1.y),
+                         pack_bf16x2(bf16lo(yy.w) + d1.z, bf16hi(yy.w) + d1.w)});
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else if (PERSIST && nitem < sc.total) {
+      tv = token_of(nit, nsv);   // a padding item: only the next item's tokens
     }
-    __builtin_amdgcn_wave_barrier();
+    if (!PERSIST || nitem >= sc.total) break;
+    __syncthreads();   // tok, h and the staging tiles are reused
+    item = nitem;
+    it = nit;
+    sv[0] = nsv[0];
+    sv[1] = nsv[1];
+    sv[2] = nsv[2];
   }
 }
 
 namespace {
+
+// Workgroups of `threads` threads of `kernel` resident at once on the current
+// device (all CUs), at least 8.
+template <typename K>
+int64_t resident_blocks(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 8;
+  return std::max<int64_t>(8, (int64_t)cus * per_cu);
+}
 
 int rt_of(int R) {
   const int RT = (R + 15) / 16;
@@ -619,11 +674,25 @@ hipError_t launch_sgmv_expand(void* y, int T, const SliceTable& st, const float*
   int nck = 0;
   for (int i = 0; i < st.n; ++i) nck += (st.off[i + 1] - st.off[i] + kCC - 1) / kCC;
   const int64_t items = (int64_t)((nck + 7) & ~7) * ((T + kBMe - 1) / kBMe + slots);
-  const int64_t grid = 8 * ((items + 7) / 8);
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  // fewer than two token blocks per slot on average: most items are short and
+  // one resident round of workgroups (a multiple of 8) loops over them
+  const bool persist = (int64_t)T < (int64_t)2 * kBMe * slots;
 #define L(RTV)                                                                                 \
-  hipLaunchKernelGGL(k_sgmv_expand<RTV>, dim3((unsigned)grid), dim3(256), 0, stream, y, T, st, \
-                     h, b, slots, R, order, indptr, ranks, scalings, min_len)
+  do {                                                                                         \
+    if (persist) {                                                                             \
+      const int64_t grid =                                                                     \
+          8 * ((std::min<int64_t>(items, resident_blocks(k_sgmv_expand<RTV, true>, 256)) + 7) / \
+               8);                                                                             \
+      hipLaunchKernelGGL((k_sgmv_expand<RTV, true>), dim3((unsigned)grid), dim3(256), 0,       \
+                         stream, y, T, st, h, b, slots, R, order, indptr, ranks, scalings,     \
+                         min_len);                                                             \
+    } else {                                                                                   \
+      hipLaunchKernelGGL((k_sgmv_expand<RTV, false>), dim3((unsigned)(8 * ((items + 7) / 8))),  \
+                         dim3(256), 0, stream, y, T, st, h, b, slots, R, order, indptr, ranks,  \
+                         scalings, min_len);                                                   \
+    }                                                                                          \
+  } while (0)
   switch (rt_of(R)) {
     case 1: L(1); break;
     case 2: L(2); break;
