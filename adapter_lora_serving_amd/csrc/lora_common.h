@@ -179,69 +179,13 @@ __device__ __forceinline__ SlotItem locate_item(int item, int slots, CountFn cou
   return r;
 }
 
-// As locate_item, with the item chosen from the total: item = pick(total)
-// (the same value in every thread; negative for none). Each slot's values
-// are loaded once by info(s, v) (three ints: segment begin, length, rank)
-// and its item count is count_of(v). When slots <= blockDim.x every thread
-// holds at most one slot and keeps its values in registers, so a workgroup
-// learns its item, and the item's slot values, after a single round of
-// loads; they are left in scratch[20..22] (read them after the call, before
-// scratch is reused).
-template <typename PickFn, typename InfoFn, typename CountFn>
-__device__ __forceinline__ SlotItem locate_picked(PickFn pick, int slots, InfoFn info,
-                                                  CountFn count_of,
-                                                  int* scratch /* >= 24 ints LDS */) {
-  const int nthreads = blockDim.x;
-  const int chunk = (slots + nthreads - 1) / nthreads;
-  const int s0 = threadIdx.x * chunk;
-  const int s1 = min(slots, s0 + chunk);
-  int v0[3] = {0, 0, 0};   // values of slot s0
-  int local = 0;
-  int first = 0;
-  for (int s = s0; s < s1; ++s) {
-    int v[3];
-    info(s, v);
-    const int c = count_of(v);
-    if (s == s0) {
-      first = c;
-      v0[0] = v[0]; v0[1] = v[1]; v0[2] = v[2];
-    }
-    local += c;
-  }
-  int total = 0;
-  const int excl = block_exclusive_scan(local, scratch, &total);
-  const int item = pick(total);
-  if (threadIdx.x == 0) { scratch[18] = -1; scratch[19] = 0; }
-  __syncthreads();
-  if (item >= 0 && item >= excl && item < excl + local) {
-    int run = excl;
-    for (int s = s0; s < s1; ++s) {
-      int v[3] = {v0[0], v0[1], v0[2]};
-      if (s != s0) info(s, v);
-      const int c = s == s0 ? first : count_of(v);
-      if (item < run + c) {
-        scratch[18] = s;
-        scratch[19] = item - run;
-        scratch[20] = v[0];
-        scratch[21] = v[1];
-        scratch[22] = v[2];
-        break;
-      }
-      run += c;
-    }
-  }
-  __syncthreads();
-  SlotItem r{scratch[18], scratch[19], total};
-  __syncthreads();
-  return r;
-}
-
-// Slot scan kept in registers for a workgroup that locates several items
-// (a grid-stride loop): scan_slots loads each slot's values once and forms
-// the block-wide exclusive prefix of the per-slot item counts; pick_item then
-// finds any item's slot without another scan. Same contract as
-// locate_picked: info(s, v) loads (segment begin, length, rank) and
-// count_of(v) gives the slot's items.
+// Work-item location in two steps, for a workgroup that locates one item or
+// several (a grid-stride loop). scan_slots loads each slot's values once
+// (info(s, v): segment begin, length, rank) and forms the block-wide
+// exclusive prefix of the per-slot item counts (count_of(v)); pick_item then
+// finds any item's slot and the slot's values without another scan. When
+// slots <= blockDim.x every thread holds at most one slot, in registers, so
+// a pick makes no memory access.
 struct SlotScan {
   int s0, s1;    // this thread's slots [s0, s1)
   int excl;      // items before slot s0

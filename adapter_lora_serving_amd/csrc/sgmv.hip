@@ -101,23 +101,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
-  const SlotItem it = locate_picked(
-      [&](int total) { return block_item(total); }, slots,
-      [&](int ss, int* v) {
-        segment_of(indptr, ss, T, v[0], v[1]);
-        v[2] = clamp_rank(ranks[ss], R);
-      },
-      [&](const int* v) {
-        if (v[1] <= min_len || v[2] <= 0) return 0;
-        const int g = shrink_group(v[2], RT, S, gmax);
-        return (S + g - 1) / g * kparts * ((v[1] + kBMs - 1) / kBMs);
-      },
-      scratch);
-  if (it.slot < 0) return;
+  auto info = [&](int ss, int* v) {
+    segment_of(indptr, ss, T, v[0], v[1]);
+    v[2] = clamp_rank(ranks[ss], R);
+  };
+  auto count_of = [&](const int* v) {
+    if (v[1] <= min_len || v[2] <= 0) return 0;
+    const int g = shrink_group(v[2], RT, S, gmax);
+    return (S + g - 1) / g * kparts * ((v[1] + kBMs - 1) / kBMs);
+  };
+  const SlotScan sc = scan_slots(slots, info, count_of, scratch);
+  if ((int)blockIdx.x >= sc.total) return;
+  __syncthreads();   // the scan's scratch is reused by the pick
+  SlotItem it;
+  int sv[3];
+  pick_item(sc, (int)blockIdx.x, info, count_of, scratch, it, sv);
   const int s = it.slot;
-  const int seg0 = scratch[20];
-  const int n = scratch[21];
-  const int r = scratch[22];
+  const int seg0 = sv[0];
+  const int n = sv[1];
+  const int r = sv[2];
   const int nmb = (n + kBMs - 1) / kBMs;
   const int kp = it.local % kparts;
   const int rest = it.local / kparts;
