@@ -29,6 +29,9 @@
 // long row-major runs; the chunk count per token block is padded to a
 // multiple of 8 so chunk ck always runs on XCD ck % 8 and its B tile stays in
 // that XCD's L2. A shrink item's K parts are innermost for the same reason.
+// For a batch of mostly short segments the expand launches one resident
+// round of workgroups (a multiple of 8) that walk the items with a grid
+// stride, so item i still runs on XCD i % 8.
 #include "lora_common.h"
 #include "lora_kernels.h"
 
