@@ -347,7 +347,7 @@ __device__ __forceinline__ void expand_group(rsrc_t y_r, int r, int lo, int ntil
                              ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
                              : kOOB;
     const u32x2 yy = yv[u];
-    bstore8(y_r, off,
+    bstore8_out(y_r, off,
             u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
                   pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])});
   }

@@ -577,12 +577,13 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
           const f32x4 d1 = *(const f32x4*)(sw + row * SRW + 8 * ppc + 4);
           const u32x4 yy = yv[q][hh];
           const int t = tok[q * 16 + row];
-          bstore16(y_r,
-                   (pcol && t >= 0) ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u : kOOB,
-                   u32x4{pack_bf16x2(bf16lo(yy.x) + d0.x, bf16hi(yy.x) + d0.y),
-                         pack_bf16x2(bf16lo(yy.y) + d0.z, bf16hi(yy.y) + d0.w),
-                         pack_bf16x2(bf16lo(yy.z) + d1.x, bf16hi(yy.z) + d1.y),
-                         pack_bf16x2(bf16lo(yy.w) + d1.z, bf16hi(yy.w) + d1.w)});
+          bstore16_out(y_r,
+                       (pcol && t >= 0) ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
+                                        : kOOB,
+                       u32x4{pack_bf16x2(bf16lo(yy.x) + d0.x, bf16hi(yy.x) + d0.y),
+                             pack_bf16x2(bf16lo(yy.y) + d0.z, bf16hi(yy.y) + d0.w),
+                             pack_bf16x2(bf16lo(yy.z) + d1.x, bf16hi(yy.z) + d1.y),
+                             pack_bf16x2(bf16lo(yy.w) + d1.z, bf16hi(yy.w) + d1.w)});
         }
         __builtin_amdgcn_wave_barrier();
       }
