@@ -271,6 +271,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// Streamed (nt) load, for data this kernel reads exactly once.
+__device__ __forceinline__ u32x4 bload16_once(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
 __device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
@@ -289,7 +293,9 @@ __device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
 // Stores of y, which the kernel writes once and never reads back: cache
 // policy sc1 | nt (streamed toward memory). Measured on the decode apply
 // (24 MB per launch): 12.9 -> 12.5 us against plain stores; nt or sc1 alone,
-// or streamed loads of x, A, B or y, gave nothing or lost time.
+// or streamed loads of x, A, B or y there, gave nothing or lost time. The
+// h written for the next kernel stays on the default policy (streaming it
+// cost the prefill expand 4-5 us).
 constexpr int kStreamOut = 18;
 __device__ __forceinline__ void bstore8_out(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kStreamOut);

@@ -476,7 +476,9 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int t = tok[q * 16 + prow + 8 * hh];
-          yv[q][hh] = bload16(y_r, (pcol && t >= 0)
+          // y rows are read once (streamed: gate/up -4.5 us; the decode's
+          // y prefetch lost time with it)
+          yv[q][hh] = bload16_once(y_r, (pcol && t >= 0)
                                        ? ((uint32_t)t * (uint32_t)out + cw + 8 * ppc) * 2u
                                        : kOOB);
         }
