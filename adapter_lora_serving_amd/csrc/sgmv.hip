@@ -90,7 +90,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
     int64_t part_stride, int min_len, int gmax) {
   constexpr int RP = RT * 16;
   constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
-  constexpr int D = RT >= 8 ? 2 : RT >= 4 ? 3 : kD;   // chunks in flight (register budget)
+  // chunks in flight: 2 from 4 rank tiles up (measured at 4: prefill down
+  // 106 -> 101 us against 3; at 8 a third chunk more than doubled the skewed
+  // mix's time)
+  constexpr int D = RT >= 4 ? 2 : kD;
   // XL: x rows are loaded as 8 rows x 128 contiguous bytes per instruction
   // and turned into the MFMA operand layout through a per-wave LDS tile
   // (16 rows x 64 bytes per instruction otherwise); the tile's 18 KB would
