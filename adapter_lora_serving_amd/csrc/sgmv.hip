@@ -324,9 +324,11 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   segment_of(indptr, s, T, b0, n);
   if (n <= min_len || clamp_rank(ranks[s], R) == 0) return;
   const int64_t off = (int64_t)token_at(order, p, T) * SR + c;
-  f32x4 v = *(const f32x4*)(part + off);
+  // each part is read once: streamed (the skewed mix -1.2 us)
+  f32x4 v = __builtin_nontemporal_load((const f32x4*)(part + off));
   for (int k = 1; k < kparts; ++k) {
-    const f32x4 u = *(const f32x4*)(part + (int64_t)k * part_stride + off);
+    const f32x4 u =
+        __builtin_nontemporal_load((const f32x4*)(part + (int64_t)k * part_stride + off));
     v = f32x4{v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w};
   }
   *(f32x4*)(h + off) = v;
