@@ -40,11 +40,6 @@ namespace {
 
 constexpr int kMT = 16;               // tokens per block (MFMA M / N tile)
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) {
-  return __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-}
-__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
-
 
 // LDS layout of one workgroup of NW waves (bytes):
 //   [0, 64)        tok[16]     token index per block row, -1 for padding

@@ -41,17 +41,10 @@ namespace lora {
 
 namespace {
 
-
 constexpr int kBMe = 64;      // tokens per expand item
 constexpr int kCC = 256;      // output columns per expand item
 constexpr int kKC = 64;       // K elements per staged chunk
 constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
-
-
-// Item of block b among n items; -1 past the end.
-__device__ __forceinline__ int block_item(int n) {
-  return (int)blockIdx.x < n ? (int)blockIdx.x : -1;
-}
 
 }  // namespace
 
@@ -376,7 +369,6 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
   __shared__ __attribute__((aligned(16))) float stage[4][16 * SRW];
 
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const int w = wave_id();
   const int S = st.n;
   const int out = st.off[S];
@@ -422,7 +414,6 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(void* __restrict__ y_, int 
     const int prow = lane_i >> 3;
     const int ppc = lane_i & 7;
     const int s = it.slot;
-    const int seg0 = sv[0];
     const int n = sv[1];
     const int r = sv[2];
     const int mb = it.local / nck8;
