@@ -284,9 +284,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
       if (++rt == ntr) { rt = 0; ++j; }
     }
   }
-  // columns [16 ntr, R) of each slice: zeros (rank rows past r)
+  // columns [16 ntr, R) of each slice: zeros (rank rows past r); with K
+  // parts k_sum_parts writes them into h and the parts never hold them
   const int zc = R - 16 * ntr;
-  if (zc > 0) {
+  if (zc > 0 && kparts == 1) {
     for (int idx = lane; idx < 16 * gsz * zc; idx += kWave) {
       const int q = idx / (gsz * zc);
       const int rem = idx - q * gsz * zc;
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
 }
 
 // h[t, :] = sum over kp (in order) of part[kp][t, :], for the tokens of
-// segments longer than min_len (the only rows the parts hold).
+// segments longer than min_len (the only rows the parts hold); the columns
+// of each slice from the slot's last rank tile on are written as zeros.
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int kparts,
                                                    int64_t part_stride, float* __restrict__ h,
                                                    int T, int SR, int slots, int R,
@@ -315,8 +317,14 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   if (s >= slots) return;
   int b0, n;
   segment_of(indptr, s, T, b0, n);
-  if (n <= min_len || clamp_rank(ranks[s], R) == 0) return;
+  const int r = clamp_rank(ranks[s], R);
+  if (n <= min_len || r == 0) return;
   const int64_t off = (int64_t)token_at(order, p, T) * SR + c;
+  // columns at or past the slot's last rank tile: zeros, not held by the parts
+  if (c % R >= 16 * ((r + 15) / 16)) {
+    *(f32x4*)(h + off) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
   // each part is read once: streamed (the skewed mix -1.2 us)
   f32x4 v = __builtin_nontemporal_load((const f32x4*)(part + off));
   for (int k = 1; k < kparts; ++k) {
