@@ -186,21 +186,38 @@ def test_linear_full_size_sampled(k, name, fused):
     assert_tol(yg[idx], y_ref, f"config {k} {name} sampled")
 
 
-def test_shrink_k_parts():
+SHRINK_KPARTS_CASES = {
+    # every slot at rank R
+    "gate_up": (3, dict(T=1024, in_features=4096, inter=1024), "gate_up"),
+    # mixed ranks over three slices: the parts hold only each slot's live
+    # rank tiles and the sum writes the columns past them as zeros
+    "mixed_ranks": (5, dict(T=1280, in_features=2304, slots=24, out_slices=(256, 128, 128)),
+                    None),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SHRINK_KPARTS_CASES))
+def test_shrink_k_parts(case):
     """lora_shrink with a workspace (K split into parts, summed in order)
     against the oracle, against the same call without one (one part), and
-    against itself (bit for bit)."""
-    log("shrink K parts")
+    against itself (bit for bit); every entry of h is written (the output
+    starts as NaN)."""
+    log(f"shrink K parts {case}")
     t = torch()
-    wl = W.make_config(3, 1, T=1024, in_features=4096, inter=1024)
-    tg = wl.target("gate_up")
+    k, over, target = SHRINK_KPARTS_CASES[case]
+    wl = W.make_config(k, 1, **over)
+    tg = wl.target(target)
+    in_f = tg.in_features
     g = GpuTarget(wl, tg)
     addr = g.addressing()
-    assert L.lib().lora_shrink_workspace_bytes(wl.T, 4096, 2, wl.R) > 0
-    h1 = L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices)
-    h2 = L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices)
-    h0 = t.empty_like(h1)
-    st = L.lib().lora_shrink(1, g.x.data_ptr(), wl.T, 4096, g.a.data_ptr(), wl.slots,
+    assert L.lib().lora_shrink_workspace_bytes(wl.T, in_f, tg.num_slices, wl.R) > 0
+    nan = float("nan")
+    h1 = t.full((wl.T, tg.num_slices * wl.R), nan, dtype=t.float32, device="cuda:0")
+    h2 = t.full_like(h1, nan)
+    L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices, out=h1)
+    L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices, out=h2)
+    h0 = t.full_like(h1, nan)
+    st = L.lib().lora_shrink(1, g.x.data_ptr(), wl.T, in_f, g.a.data_ptr(), wl.slots,
                              tg.num_slices, wl.R, addr.token_order.data_ptr(),
                              addr.slot_indptr.data_ptr(), g.ranks.data_ptr(), h0.data_ptr(),
                              None, 0, t.cuda.current_stream().cuda_stream)
