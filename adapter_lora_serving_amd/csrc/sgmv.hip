@@ -61,7 +61,7 @@ constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
 // [j * ntr, (j + 1) * ntr). gmax keeps a group's A rows below 2 GiB.
 // With kparts > 1 each item writes its partial h to its own buffer
 // (hout + kp * part_stride); k_sum_parts adds them in kp order. Every item
-// writes all R columns of each of its slices (zeros from ntr * 16 on).
+// writes the columns of its slices below 16 * ntr.
 constexpr int kBMs = 128;
 constexpr int kD = 4;
 
@@ -284,23 +284,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
       if (++rt == ntr) { rt = 0; ++j; }
     }
   }
-  // columns [16 ntr, R) of each slice: zeros (rank rows past r); with K
-  // parts k_sum_parts writes them into h and the parts never hold them
-  const int zc = R - 16 * ntr;
-  if (zc > 0 && kparts == 1) {
-    for (int idx = lane; idx < 16 * gsz * zc; idx += kWave) {
-      const int q = idx / (gsz * zc);
-      const int rem = idx - q * gsz * zc;
-      const int j = rem / zc;
-      const int tt = tok[w * 16 + q];
-      if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + 16 * ntr + (rem - j * zc)] = 0.f;
-    }
-  }
+  // columns [16 ntr, R) of each slice are not written: lora_shrink's VALU
+  // kernel writes the zeros of h, and lora_apply_linear's h is read only
+  // below the rank
 }
 
 // h[t, :] = sum over kp (in order) of part[kp][t, :], for the tokens of
-// segments longer than min_len (the only rows the parts hold); the columns
-// of each slice from the slot's last rank tile on are written as zeros.
+// segments longer than min_len (the only rows the parts hold), over each
+// slice's columns below the slot's last rank tile.
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int kparts,
                                                    int64_t part_stride, float* __restrict__ h,
                                                    int T, int SR, int slots, int R,
@@ -318,13 +309,10 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ par
   int b0, n;
   segment_of(indptr, s, T, b0, n);
   const int r = clamp_rank(ranks[s], R);
-  if (n <= min_len || r == 0) return;
+  // columns at or past the slot's last rank tile are neither in the parts
+  // nor written (see the shrink)
+  if (n <= min_len || r == 0 || c % R >= 16 * ((r + 15) / 16)) return;
   const int64_t off = (int64_t)token_at(order, p, T) * SR + c;
-  // columns at or past the slot's last rank tile: zeros, not held by the parts
-  if (c % R >= 16 * ((r + 15) / 16)) {
-    *(f32x4*)(h + off) = f32x4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
   // each part is read once: streamed (the skewed mix -1.2 us)
   f32x4 v = __builtin_nontemporal_load((const f32x4*)(part + off));
   for (int k = 1; k < kparts; ++k) {
