@@ -810,10 +810,14 @@ int decode_chunk_cols(int R) {
   return R <= 32 ? 1024 : 2048;
 }
 
-int k_parts(int in) {
-  // K parts of a decode shrink (each ~2048 deep); overridable for tuning
+int k_parts(int in, int out) {
+  // K parts of a decode shrink: ~2048 deep, or ~1024 when the output is
+  // narrower than one expand chunk (a router's logits: then every slot has a
+  // single expand piece, and more, shorter shrink pieces shorten the chain:
+  // measured at 64 outputs, 9.5 -> 8.1 us for 2 -> 4 parts; 8 parts 9.4 us);
+  // overridable for tuning
   const int env = env_int("LORA_KPARTS", 0);
-  int kp = env > 0 ? env : in / 2048;
+  int kp = env > 0 ? env : in / (out < 1024 ? 1024 : 2048);
   return kp < 1 ? 1 : kp > 8 ? 8 : kp;
 }
 
@@ -859,7 +863,8 @@ size_t counter_bytes(int slots, int S) {
 
 size_t fused_partial_bytes(int slots, int S, int R, int in) {
   const int RP = rt_bucket(R) * 16;
-  return (size_t)slots * S * k_parts(in) * kMT * RP * 4;
+  // room for the most parts any output width takes
+  return (size_t)slots * S * k_parts(in, 0) * kMT * RP * 4;
 }
 
 bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in) {
@@ -883,7 +888,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const ChunkTable ct = make_chunks(st, R);
-  const int KP = k_parts(in);
+  const int KP = k_parts(in, st.off[st.n]);
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
   // rank classes (largest first) where ranks differ enough to matter
   const int nclass = rt_bucket(R) >= 4 ? 3 : 1;

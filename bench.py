@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="synthetic workload 1-5 (default 2)")
     ap.add_argument("--target", default=None, help="target name for multi-target workloads")
+    ap.add_argument("--workload", choices=["router_fold"], default=None,
+                    help="a workload beyond the five configs: router_fold (a router LoRA "
+                         "folded onto 64 routing logits, decode batch)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -132,7 +135,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl = W.make_config(args.config, seed=0)
+    wl = W.make_router_fold(0) if args.workload == "router_fold" else W.make_config(args.config,
+                                                                                   seed=0)
     tg = wl.target(args.target)
     alg_bytes, alg_flops, terms = workload_cost(wl, tg)
     eb = 2 if wl.dtype == "bf16" else 4

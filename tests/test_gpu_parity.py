@@ -394,6 +394,31 @@ def test_edge_cases(case, fused):
     assert np.array_equal(f64(y)[same], O.decode(tg.y0, wl.dtype)[same])
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_router_fold(size, fused):
+    """A router LoRA folded onto the routing logits before top-k (one out
+    slice of 64 experts on the router input), small and at its full decode
+    size, against the oracle."""
+    log(f"router fold {size} fused={fused}")
+    over = dict(T=64, hidden=512) if size == "small" else {}
+    wl = W.make_router_fold(3, **over)
+    tg = wl.targets[0]
+    assert tg.out_slices == (64,)
+    _, _, y = GpuTarget(wl, tg).run(fused=fused)
+    _, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, f"router {size}")
+
+
+def test_router_fold_f32():
+    """The same fold on float32 logits (the VALU kernels)."""
+    wl = W.make_router_fold(4, T=64, hidden=256, dtype="f32")
+    tg = wl.targets[0]
+    _, _, y = GpuTarget(wl, tg).run(fused=True)
+    _, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, "router f32")
+
+
 def test_T0_is_noop():
     t = torch()
     wl = _custom(1, T=8, in_f=64, out_slices=(16,), R=8, slots=2, ranks=[8, 8])

@@ -174,6 +174,26 @@ CONFIG_NAMES = {
 }
 
 
+ROUTER_FOLD = "router_fold_bf16"
+
+
+def make_router_fold(seed: int = 0, *, T: int = 256, hidden: int = 4096, num_experts: int = 64,
+                     slots: int = 32, dtype: str = "bf16", y0_zero: bool = False) -> Workload:
+    """A router LoRA folded onto the routing logits before top-k: one linear
+    target with a single out slice of num_experts columns on the router
+    input. The pages give no sizes; this takes the decode batch of the
+    qkv workload (T=256 one-token requests over 32 slots, ranks 8 or 16,
+    scaling 2.0, x, A, B Gaussian as there) with 64 experts."""
+    rng = np.random.default_rng(seed)
+    ranks = rng.choice(np.array([8, 16]), size=slots)
+    scal = np.full(slots, 2.0, np.float32)
+    tslot = rng.integers(0, slots, size=T, dtype=np.int64)
+    return make_workload(name=ROUTER_FOLD if dtype == "bf16" else "router_fold_f32", dtype=dtype,
+                         T=T, in_features=hidden, out_slices=(num_experts,), R=16, slots=slots,
+                         ranks=ranks, scalings=scal, token_slot=tslot, seed=seed, rng=rng,
+                         y0_zero=y0_zero, target_name="router")
+
+
 def make_config(k: int, seed: int = 0, *, y0_zero: bool = False, **over) -> Workload:
     """The five synthetic workloads of the hot path, seeded.
 
