@@ -113,9 +113,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="synthetic workload 1-5 (default 2)")
     ap.add_argument("--target", default=None, help="target name for multi-target workloads")
-    ap.add_argument("--workload", choices=["router_fold"], default=None,
+    ap.add_argument("--workload", choices=["router_fold", "tp8_qkv_decode", "tp8_prefill"],
+                    default=None,
                     help="a workload beyond the five configs: router_fold (a router LoRA "
-                         "folded onto 64 routing logits, decode batch)")
+                         "folded onto 64 routing logits, decode batch); tp8_qkv_decode, "
+                         "tp8_prefill (one GPU's share of a TP=8 projection; --target "
+                         "gate_up or down for the latter)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,8 +138,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wl = W.make_router_fold(0) if args.workload == "router_fold" else W.make_config(args.config,
-                                                                                   seed=0)
+    if args.workload == "router_fold":
+        wl = W.make_router_fold(0)
+    elif args.workload in W.TP_SHARES:
+        wl = W.make_tp_share(args.workload, 0)
+    else:
+        wl = W.make_config(args.config, seed=0)
     tg = wl.target(args.target)
     alg_bytes, alg_flops, terms = workload_cost(wl, tg)
     eb = 2 if wl.dtype == "bf16" else 4

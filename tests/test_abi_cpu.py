@@ -83,7 +83,9 @@ def test_shrink_validation(lib):
     assert need == 4 * 16 * 4 * 4                  # 4 parts of a [4, 16] float32 h
     assert call(inf=4096, ws=A16, wsb=need - 1) == WORKSPACE
     assert call(inf=4096, ws=A16 + 16, wsb=need) == ALIGN
-    assert lib.lora_shrink_workspace_bytes(4, 1024, 1, 16) == 0    # too shallow to split
+    # a shallow `in` still takes 4 parts of >= 256; below 512 one part, no workspace
+    assert lib.lora_shrink_workspace_bytes(4, 1024, 1, 16) == 4 * 16 * 4 * 4
+    assert lib.lora_shrink_workspace_bytes(4, 256, 1, 16) == 0
     assert lib.lora_shrink_workspace_bytes(-1, 4096, 1, 16) == 0   # bad input
 
 

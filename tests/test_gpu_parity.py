@@ -410,6 +410,41 @@ def test_router_fold(size, fused):
     assert_tol(f64(y), y_ref, f"router {size}")
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_tp8_qkv_decode_share(fused):
+    """One GPU's column share of the qkv decode projection at TP = 8 (out
+    slices 512, 128, 128), whole, against the oracle."""
+    log(f"tp8 qkv decode share fused={fused}")
+    wl = W.make_tp_share("tp8_qkv_decode", 2)
+    tg = wl.targets[0]
+    assert tg.out_slices == (512, 128, 128)
+    _, _, y = GpuTarget(wl, tg).run(fused=fused)
+    _, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, "tp8 qkv share")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_tp8_prefill_share_sampled(name):
+    """One GPU's share of the prefill projections at TP = 8 (gate/up: out
+    slices 1792 each; down: in 1792), full size, on sampled rows."""
+    log(f"tp8 prefill share {name}")
+    wl = W.make_tp_share("tp8_prefill", 0)
+    tg = wl.target(name)
+    _, _, y = GpuTarget(wl, tg).run(fused=True)
+    yg = f64(y)
+    order, indptr = O.build_addressing(wl.token_slot, wl.slots)
+    pick = set()
+    for s in range(wl.slots):
+        if indptr[s + 1] > indptr[s]:
+            pick.update([int(order[indptr[s]]), int(order[indptr[s + 1] - 1])])
+    pick.update(np.random.default_rng(6).choice(wl.T, size=24, replace=False).tolist())
+    idx = np.array(sorted(pick))
+    sub = W.take_tokens(wl, idx)
+    _, y_ref = O.run_target(sub, sub.target(name))
+    assert_tol(yg[idx], y_ref, f"tp8 prefill share {name}")
+
+
 def test_router_fold_f32():
     """The same fold on float32 logits (the VALU kernels)."""
     wl = W.make_router_fold(4, T=64, hidden=256, dtype="f32")

@@ -194,6 +194,27 @@ def make_router_fold(seed: int = 0, *, T: int = 256, hidden: int = 4096, num_exp
                          y0_zero=y0_zero, target_name="router")
 
 
+TP_SHARES = ("tp8_qkv_decode", "tp8_prefill")
+
+
+def make_tp_share(name: str, seed: int = 0) -> Workload:
+    """One GPU's share of a tensor-parallel projection at TP = 8, at its real
+    shape: column-parallel targets keep x and A whole and take an eighth of
+    every out slice (B's rows); row-parallel targets take an eighth of `in`
+    (x's columns and A's). tp8_qkv_decode: the qkv decode workload with out
+    slices (512, 128, 128). tp8_prefill: the prefill workload with an
+    intermediate width of 1792, so gate/up is the column share (1792, 1792)
+    and down the row share (in 1792)."""
+    if name == "tp8_qkv_decode":
+        wl = make_config(2, seed, out_slices=(4096 // 8, 1024 // 8, 1024 // 8))
+    elif name == "tp8_prefill":
+        wl = make_config(3, seed, inter=14336 // 8)
+    else:
+        raise ValueError(f"unknown share {name}")
+    wl.name = name + "_bf16"
+    return wl
+
+
 def make_config(k: int, seed: int = 0, *, y0_zero: bool = False, **over) -> Workload:
     """The five synthetic workloads of the hot path, seeded.
 
