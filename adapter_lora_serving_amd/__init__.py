@@ -43,6 +43,9 @@ SIGNATURES = {
     "lora_version": (ctypes.c_char_p, []),
     "lora_build_addressing": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "lora_build_addressing_workspace_bytes": (_SZ, [_I64, _I32]),
+    "lora_build_addressing_experts": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _P, _P, _P, _SZ,
+                                                     _P]),
+    "lora_build_addressing_experts_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "lora_shrink": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P,
                                    _P, _P, _P, _SZ, _P]),
     "lora_shrink_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
@@ -149,6 +152,32 @@ def build_addressing(token_slot, slots: int, out: Optional[Addressing] = None) -
     st = lib().lora_build_addressing(_ptr(token_slot), T, slots, _ptr(out.token_order),
                                      _ptr(out.slot_indptr), _ptr(ws), nws, _stream(dev))
     _check(st, "lora_build_addressing")
+    return out
+
+
+def build_addressing_experts(row_slot, expert_offsets, num_experts: int, slots: int,
+                             out: Optional[Addressing] = None) -> Addressing:
+    """Group the rows of an expert-sorted batch by (expert, slot) on the
+    device; virtual slot k = expert * slots + slot (num_experts * slots of
+    them)."""
+    import torch
+    row_slot = _i32(row_slot)
+    expert_offsets = _i32(expert_offsets)
+    dev = _dev(row_slot, expert_offsets)
+    rows = row_slot.numel()
+    if expert_offsets.numel() != num_experts + 1:
+        raise LoraError("expert_offsets must hold num_experts + 1 entries")
+    if out is None:
+        out = Addressing(torch.empty(rows, dtype=torch.int32, device=dev),
+                         torch.empty(num_experts * slots + 1, dtype=torch.int32, device=dev))
+    _dev(row_slot, *out)
+    nws = int(lib().lora_build_addressing_experts_workspace_bytes(rows, num_experts, slots))
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    st = lib().lora_build_addressing_experts(_ptr(row_slot), _ptr(expert_offsets), num_experts,
+                                             rows, slots, _ptr(out.token_order),
+                                             _ptr(out.slot_indptr), _ptr(ws), ws.numel(),
+                                             _stream(dev))
+    _check(st, "lora_build_addressing_experts")
     return out
 
 

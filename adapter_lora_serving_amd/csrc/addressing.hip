@@ -286,6 +286,29 @@ size_t addressing_lds_bytes(int nw, int slots) {
   return (size_t)((nw + 1) * (slots + 1) + 20) * sizeof(int);
 }
 
+// Composite key of each row of an expert-sorted batch: expert e of row r is
+// the e with offs[e] <= r < offs[e + 1]; key = e * slots + row_slot[r], or
+// -1 (dead) for a slot outside [0, slots) or a row outside [offs[0],
+// offs[E]). A malformed offs gives wrong keys but no access out of bounds.
+__global__ __launch_bounds__(256) void k_expert_keys(const int32_t* __restrict__ row_slot,
+                                                     const int32_t* __restrict__ offs, int E,
+                                                     int rows, int slots,
+                                                     int32_t* __restrict__ keys) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  int key = -1;
+  if (r >= offs[0] && r < offs[E]) {
+    int lo = 0, hi = E;   // invariant: offs[lo] <= r < offs[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offs[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int s = row_slot[r];
+    if (s >= 0 && s < slots) key = lo * slots + s;
+  }
+  keys[r] = key;
+}
+
 size_t addressing_workspace_bytes(int64_t T, int slots) {
   // the two-pass path: batches past one block, keys within one per thread
   if (T <= kBlockTok || slots + 1 > kBlockTok) return 0;
@@ -346,6 +369,27 @@ hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
   hipLaunchKernelGGL(k_build_addressing, dim3(1), dim3(nw * kWave), lds, stream, token_slot, T,
                      slots, token_order, slot_indptr);
   return hipGetLastError();
+}
+
+size_t expert_addressing_workspace_bytes(int64_t rows, int E, int slots) {
+  const size_t keys = ((size_t)rows * sizeof(int32_t) + 255) & ~(size_t)255;
+  return keys + addressing_workspace_bytes(rows, E * slots);
+}
+
+hipError_t launch_build_addressing_experts(const int32_t* row_slot, const int32_t* offs, int E,
+                                           int rows, int slots, int32_t* token_order,
+                                           int32_t* slot_indptr, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  const size_t kb = ((size_t)rows * sizeof(int32_t) + 255) & ~(size_t)255;
+  int32_t* keys = (int32_t*)ws;
+  if (rows > 0) {
+    hipLaunchKernelGGL(k_expert_keys, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                       row_slot, offs, E, rows, slots, keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_build_addressing(keys, rows, E * slots, token_order, slot_indptr,
+                                 (char*)ws + kb, ws_bytes - kb, stream);
 }
 
 }  // namespace lora

@@ -108,6 +108,32 @@ lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t 
                                                   (hipStream_t)stream));
 }
 
+size_t lora_build_addressing_experts_workspace_bytes(int64_t rows, int32_t num_experts,
+                                                     int32_t slots) {
+  if (rows < 0 || rows > kMaxI32 || num_experts < 1 || slots < 1 ||
+      (int64_t)num_experts * slots > 8192)
+    return 0;
+  return lora::expert_addressing_workspace_bytes(rows, num_experts, slots);
+}
+
+lora_status lora_build_addressing_experts(const int32_t* row_slot, const int32_t* expert_offsets,
+                                          int32_t num_experts, int64_t rows, int32_t slots,
+                                          int32_t* token_order, int32_t* slot_indptr,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || rows > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (num_experts < 1 || slots < 1 || (int64_t)num_experts * slots > 8192)
+    return LORA_ERR_UNSUPPORTED;
+  if (!slot_indptr || !expert_offsets) return LORA_ERR_INVALID_ARG;
+  if (rows > 0 && (!row_slot || !token_order)) return LORA_ERR_INVALID_ARG;
+  if (!workspace ||
+      workspace_bytes < lora_build_addressing_experts_workspace_bytes(rows, num_experts, slots))
+    return LORA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  return hip_status(lora::launch_build_addressing_experts(
+      row_slot, expert_offsets, num_experts, (int)rows, slots, token_order, slot_indptr,
+      workspace, workspace_bytes, (hipStream_t)stream));
+}
+
 size_t lora_shrink_workspace_bytes(int64_t T, int64_t in_features, int32_t num_slices,
                                    int32_t R) {
   if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||

@@ -36,6 +36,15 @@ hipError_t launch_build_addressing(const int32_t* token_slot, int T, int slots,
                                    int32_t* token_order, int32_t* slot_indptr, void* ws,
                                    size_t ws_bytes, hipStream_t stream);
 
+// Addressing of an expert-sorted batch (rows grouped by expert, bounds in
+// offs[0..E]) over the composite key expert * slots + slot; the workspace
+// holds the keys, then the addressing's own workspace.
+size_t expert_addressing_workspace_bytes(int64_t rows, int E, int slots);
+hipError_t launch_build_addressing_experts(const int32_t* row_slot, const int32_t* offs, int E,
+                                           int rows, int slots, int32_t* token_order,
+                                           int32_t* slot_indptr, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+
 hipError_t launch_gather_shrink(int dtype, const int32_t* ids, int T, int64_t vocab,
                                 const void* a, int slots, int R, const int32_t* token_order,
                                 const int32_t* indptr, const int32_t* ranks, float* h,

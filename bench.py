@@ -113,12 +113,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="synthetic workload 1-5 (default 2)")
     ap.add_argument("--target", default=None, help="target name for multi-target workloads")
-    ap.add_argument("--workload", choices=["router_fold", "tp8_qkv_decode", "tp8_prefill"],
+    ap.add_argument("--workload", choices=["router_fold", "tp8_qkv_decode", "tp8_prefill",
+                                           "moe_experts"],
                     default=None,
                     help="a workload beyond the five configs: router_fold (a router LoRA "
                          "folded onto 64 routing logits, decode batch); tp8_qkv_decode, "
                          "tp8_prefill (one GPU's share of a TP=8 projection; --target "
-                         "gate_up or down for the latter)")
+                         "gate_up or down for the latter); moe_experts (the routed-expert "
+                         "LoRA on 512 expert-sorted rows, its addressing by (expert, slot))")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -140,6 +142,8 @@ def main():
 
     if args.workload == "router_fold":
         wl = W.make_router_fold(0)
+    elif args.workload == "moe_experts":
+        wl = W.make_moe_experts(0)
     elif args.workload in W.TP_SHARES:
         wl = W.make_tp_share(args.workload, 0)
     else:
@@ -168,9 +172,20 @@ def main():
     else:
         x0 = d(tg.x)
     a0, b0, y0 = d(tg.a), d(tg.b), d(tg.y0)
+    ex = getattr(wl, "experts", None)
+
+    def addressing(s, out=None):
+        if ex is None:
+            return L.build_addressing(s["ts"], wl.slots, out=out)
+        # rows of an expert-sorted batch: grouped by (expert, slot) on the device
+        return L.build_addressing_experts(s["rs"], s["offs"], ex["experts"], ex["slots"], out=out)
+
     for i in range(n_sets):
         s = dict(x=x0.clone(), a=a0.clone(), b=b0.clone(), y=y0.clone(), ts=ts_host.to(dev))
-        s["addr"] = L.build_addressing(s["ts"], wl.slots)
+        if ex is not None:
+            s["rs"] = torch.from_numpy(ex["row_slot"]).to(dev)
+            s["offs"] = torch.from_numpy(ex["offsets"]).to(dev)
+        s["addr"] = addressing(s)
         sets.append(s)
     del x0, a0, b0, y0
     if tg.embedding:
@@ -190,12 +205,12 @@ def main():
 
     def step(i):
         s = sets[i % n_sets]
-        L.build_addressing(s["ts"], wl.slots, out=s["addr"])
+        addressing(s, out=s["addr"])
         apply_only(i)
 
     def addr_only(i):
         s = sets[i % n_sets]
-        L.build_addressing(s["ts"], wl.slots, out=s["addr"])
+        addressing(s, out=s["addr"])
 
     for i in range(args.warmup):
         step(i)

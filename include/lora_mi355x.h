@@ -115,6 +115,44 @@ lora_status lora_build_addressing(const int32_t* token_slot, int64_t T, int32_t 
 size_t lora_build_addressing_workspace_bytes(int64_t T, int32_t slots);
 
 /*
+ * lora_build_addressing_experts: the addressing of a routed-expert batch.
+ *
+ * Source: page "spark_model/lora/expert_apply.rs", the experts injection
+ * shape (apply_expert_lora_sorted): the expert LoRA delta is applied to the
+ * rows of the base grouped GEMM, which are sorted by expert, each row
+ * carrying its token's adapter slot. Here the (expert, slot) pair is one
+ * composite key, expert * slots + slot, and the rows are grouped by it with
+ * the same stable counting sort as lora_build_addressing, on the device.
+ * row_slot       device int32 [rows]: adapter slot of each row; outside
+ *                [0, slots) the row is dead.
+ * expert_offsets device int32 [num_experts + 1], non-decreasing: rows
+ *                [expert_offsets[e], expert_offsets[e+1]) belong to expert
+ *                e; rows outside [expert_offsets[0], expert_offsets[E]) are
+ *                dead. A malformed array gives wrong keys, never an access
+ *                out of bounds.
+ * token_order    device int32 [rows] (out), rows grouped by key, stable.
+ * slot_indptr    device int32 [num_experts * slots + 1] (out): the rows of
+ *                (expert e, slot s) are token_order[slot_indptr[k] ..
+ *                slot_indptr[k+1]) with k = e * slots + s.
+ * The result is the addressing of the same rows with token_slot = key, for
+ * num_experts * slots virtual slots (<= 8192), whose adapter weights and
+ * ranks / scalings the apply entry points then index by k.
+ * workspace (device, required): at least
+ * lora_build_addressing_experts_workspace_bytes(rows, num_experts, slots)
+ * bytes, 256-byte aligned; contents need no initialisation; calls sharing
+ * one workspace must not overlap in time. Missing or too small:
+ * LORA_ERR_WORKSPACE.
+ */
+lora_status lora_build_addressing_experts(const int32_t* row_slot, const int32_t* expert_offsets,
+                                          int32_t num_experts, int64_t rows, int32_t slots,
+                                          int32_t* token_order, int32_t* slot_indptr,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_build_addressing_experts needs (0 on bad input). */
+size_t lora_build_addressing_experts_workspace_bytes(int64_t rows, int32_t num_experts,
+                                                     int32_t slots);
+
+/*
  * lora_shrink: h[t, i*R + j] = x[t] . a[slot(t), i*R + j] for j < rank(slot(t)).
  *
  * Source: lora.backend, LoraBackend.shrink (h[t] = x[t] @ a[slot(t)]^T) and

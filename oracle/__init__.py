@@ -1,5 +1,6 @@
 """CPU oracle (test infrastructure only): see oracle.lora_oracle."""
 from .lora_oracle import (  # noqa: F401
-    decode, build_addressing, shrink, gather_shrink, expand, apply, apply_linear,
+    decode, build_addressing, expert_keys, build_addressing_experts, shrink, gather_shrink,
+    expand, apply, apply_linear,
     shrink_all_slots, apply_scalar, run_target, within_tolerance,
 )

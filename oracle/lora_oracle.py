@@ -102,6 +102,29 @@ def build_addressing(token_slot: Sequence[int], slots: int) -> Tuple[np.ndarray,
     return np.asarray(order, dtype=np.int32), np.asarray(start[: slots + 1], dtype=np.int32)
 
 
+def expert_keys(row_slot: Sequence[int], expert_offsets: Sequence[int], num_experts: int,
+                slots: int) -> np.ndarray:
+    """Composite key of each row of an expert-sorted batch (page
+    "spark_model/lora/expert_apply.rs", the experts injection shape: rows of
+    the grouped GEMM sorted by expert, each with its token's slot): expert e
+    holds rows [offsets[e], offsets[e+1]); key = e * slots + slot, or -1 for
+    a dead row (slot outside [0, slots), or no expert)."""
+    keys = np.full(len(row_slot), -1, dtype=np.int64)
+    for e in range(num_experts):
+        for r in range(int(expert_offsets[e]), int(expert_offsets[e + 1])):
+            if 0 <= r < len(row_slot) and _live(int(row_slot[r]), slots):
+                keys[r] = e * slots + int(row_slot[r])
+    return keys
+
+
+def build_addressing_experts(row_slot: Sequence[int], expert_offsets: Sequence[int],
+                             num_experts: int, slots: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The addressing of those rows over num_experts * slots virtual slots:
+    the stable counting sort of build_addressing on the composite keys."""
+    return build_addressing(expert_keys(row_slot, expert_offsets, num_experts, slots),
+                            num_experts * slots)
+
+
 # ---------------------------------------------------------------------------
 # shrink / gather_shrink / expand
 # ---------------------------------------------------------------------------

@@ -445,6 +445,47 @@ def test_tp8_prefill_share_sampled(name):
     assert_tol(yg[idx], y_ref, f"tp8 prefill share {name}")
 
 
+@pytest.mark.parametrize("rows,E,slots", [(300, 8, 16), (2000, 8, 32), (5000, 64, 64)])
+def test_expert_addressing_bit_exact(rows, E, slots):
+    """The device addressing of an expert-sorted batch equals the oracle's,
+    bit for bit (dead rows: bad slots and rows outside the expert bounds)."""
+    t = torch()
+    rng = np.random.default_rng(rows)
+    cuts = np.sort(rng.integers(0, rows + 1, size=E - 1))
+    offs = np.concatenate([[3], cuts.clip(3, rows - 2), [rows - 2]]).astype(np.int32)
+    row_slot = rng.integers(-1, slots + 1, size=rows).astype(np.int32)
+    addr = L.build_addressing_experts(t.from_numpy(row_slot).to("cuda:0"),
+                                      t.from_numpy(offs).to("cuda:0"), E, slots)
+    t.cuda.synchronize()
+    order, indptr = O.build_addressing_experts(row_slot, offs, E, slots)
+    assert np.array_equal(addr.token_order.cpu().numpy(), order)
+    assert np.array_equal(addr.slot_indptr.cpu().numpy(), indptr)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_moe_expert_lora(fused):
+    """The routed-expert LoRA delta on expert-sorted rows: the device expert
+    addressing, then the apply over expert * slots virtual slots, against the
+    oracle."""
+    t = torch()
+    wl = W.make_moe_experts(5, T=256, experts=8, hidden=1024, inter=2048)
+    tg = wl.targets[0]
+    g = GpuTarget(wl, tg)
+    e = wl.experts
+    addr = L.build_addressing_experts(t.from_numpy(e["row_slot"]).to("cuda:0"),
+                                      t.from_numpy(e["offsets"]).to("cuda:0"), e["experts"],
+                                      e["slots"])
+    y = g.y0.clone()
+    if fused:
+        L.apply_linear_(g.x, y, g.a, g.b, addr, g.ranks, g.scal, tg.out_slices)
+    else:
+        h = L.shrink(g.x, g.a, addr, g.ranks, tg.num_slices)
+        L.expand_(h, g.b, addr, g.ranks, g.scal, y, tg.out_slices)
+    t.cuda.synchronize()
+    _, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, "moe experts")
+
+
 def test_router_fold_f32():
     """The same fold on float32 logits (the VALU kernels)."""
     wl = W.make_router_fold(4, T=64, hidden=256, dtype="f32")

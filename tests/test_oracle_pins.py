@@ -355,3 +355,24 @@ def test_pins_catch_planted_mistake(mut):
         except Exception:  # an assertion or a shape error both mean "caught"
             caught.append(pin.__name__)
     assert caught, f"no pin catches mutant {mut}"
+
+
+def test_expert_addressing_is_lexicographic_sort():
+    """The expert addressing equals a plain stable sort of the rows by
+    (expert, slot), dead rows last: checked against Python's sorted."""
+    rng = np.random.default_rng(11)
+    for rows, E, slots in ((1, 1, 1), (40, 3, 5), (300, 8, 16)):
+        cuts = np.sort(rng.integers(0, rows + 1, size=E - 1))
+        offs = np.concatenate([[0], cuts, [rows]]).astype(np.int32)
+        row_slot = rng.integers(-1, slots + 1, size=rows)
+        order, indptr = O.build_addressing_experts(row_slot, offs, E, slots)
+        expert = np.searchsorted(offs, np.arange(rows), side="right") - 1
+        live = (row_slot >= 0) & (row_slot < slots)
+        want = sorted(range(rows), key=lambda r: (0, expert[r], row_slot[r], r) if live[r]
+                      else (1, 0, 0, r))
+        assert order.tolist() == want
+        for e in range(E):
+            for sl in range(slots):
+                k = e * slots + sl
+                seg = order[indptr[k]:indptr[k + 1]]
+                assert all(expert[r] == e and row_slot[r] == sl for r in seg)

@@ -194,6 +194,45 @@ def make_router_fold(seed: int = 0, *, T: int = 256, hidden: int = 4096, num_exp
                          y0_zero=y0_zero, target_name="router")
 
 
+MOE_EXPERTS = "moe_experts_bf16"
+
+
+def make_moe_experts(seed: int = 0, *, T: int = 256, experts: int = 8, topk: int = 2,
+                     hidden: int = 4096, inter: int = 14336, slots: int = 32,
+                     y0_zero: bool = False) -> Workload:
+    """The routed-expert LoRA delta on the rows of an expert-sorted grouped
+    GEMM: each token goes to `topk` distinct experts drawn uniformly, the
+    rows (token, expert) are sorted by expert (stably, by token), and each
+    row carries its token's slot. The delta of a row uses the LoRA of
+    (expert, slot); as a linear target that is virtual slot k = expert *
+    slots + slot over experts * slots slots (A, B, ranks and scalings indexed
+    by k; a slot's rank and scaling are the same for every expert). The
+    pages give no sizes: an 8-expert, top-2 MoE with 4096 hidden and 14336
+    intermediate (the expert gate/up projection), over the decode recipe's
+    256 tokens and 32 slots. `wl.experts` holds what the device addressing
+    takes: the base slots, row_slot and expert_offsets."""
+    rng = np.random.default_rng(seed)
+    base_ranks = rng.choice(np.array([8, 16]), size=slots)
+    tok_slot = rng.integers(0, slots, size=T, dtype=np.int64)
+    route = np.stack([rng.choice(experts, size=topk, replace=False) for _ in range(T)])
+    tok = np.repeat(np.arange(T), topk)
+    ex = route.reshape(-1)
+    order = np.argsort(ex, kind="stable")
+    tok, ex = tok[order], ex[order]
+    offsets = np.concatenate([[0], np.cumsum(np.bincount(ex, minlength=experts))])
+    row_slot = tok_slot[tok]
+    keys = ex * slots + row_slot
+    vslots = experts * slots
+    wl = make_workload(name=MOE_EXPERTS, dtype="bf16", T=len(keys), in_features=hidden,
+                       out_slices=(inter, inter), R=16, slots=vslots,
+                       ranks=np.tile(base_ranks, experts),
+                       scalings=np.full(vslots, 2.0, np.float32), token_slot=keys, seed=seed,
+                       rng=rng, y0_zero=y0_zero, target_name="expert_gate_up")
+    wl.experts = dict(experts=experts, slots=slots, row_slot=row_slot.astype(np.int32),
+                      offsets=offsets.astype(np.int32))
+    return wl
+
+
 TP_SHARES = ("tp8_qkv_decode", "tp8_prefill")
 
 
