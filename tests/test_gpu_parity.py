@@ -486,6 +486,52 @@ def test_moe_expert_lora(fused):
     assert_tol(f64(y), y_ref, "moe experts")
 
 
+def test_moe_experts_graph_equals_eager():
+    """The expert addressing plus the apply recorded in a graph, replayed
+    with new row slots, matches eager execution bit for bit on every
+    replay."""
+    t = torch()
+    wl = W.make_moe_experts(6, T=96, experts=4, hidden=512, inter=256, slots=8)
+    tg = wl.targets[0]
+    g = GpuTarget(wl, tg)
+    e = wl.experts
+    rs = t.from_numpy(e["row_slot"]).to("cuda:0")
+    offs = t.from_numpy(e["offsets"]).to("cuda:0")
+    y = g.y0.clone()
+    addr = L.build_addressing_experts(rs, offs, e["experts"], e["slots"])
+
+    def step(a, yy):
+        L.apply_linear_(g.x, yy, g.a, g.b, a, g.ranks, g.scal, tg.out_slices)
+
+    step(addr, y)   # warm-up
+    t.cuda.synchronize()
+    graph = t.cuda.CUDAGraph()
+    st = t.cuda.Stream()
+    with t.cuda.stream(st):
+        y.copy_(g.y0)
+        with t.cuda.graph(graph, stream=st):
+            L.build_addressing_experts(rs, offs, e["experts"], e["slots"], out=addr)
+            step(addr, y)
+    t.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    for rep in range(3):
+        new = rng.integers(-1, e["slots"], size=wl.T).astype(np.int32)
+        rs.copy_(t.from_numpy(new))
+        y.copy_(g.y0)
+        t.cuda.synchronize()
+        graph.replay()
+        t.cuda.synchronize()
+        y_graph = y.clone()
+        y_e = g.y0.clone()
+        a_e = L.build_addressing_experts(t.from_numpy(new).to("cuda:0"), offs, e["experts"],
+                                         e["slots"])
+        step(a_e, y_e)
+        t.cuda.synchronize()
+        assert t.equal(addr.token_order, a_e.token_order)
+        assert t.equal(addr.slot_indptr, a_e.slot_indptr)
+        assert t.equal(y_graph, y_e), f"replay {rep}"
+
+
 def test_router_fold_f32():
     """The same fold on float32 logits (the VALU kernels)."""
     wl = W.make_router_fold(4, T=64, hidden=256, dtype="f32")
