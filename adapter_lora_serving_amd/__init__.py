@@ -8,8 +8,8 @@ is present, the calls raise.
 
 Names and argument order follow the LoraBackend methods of the mstar
 lora.backend page (shrink, gather_shrink, expand_fused, apply_linear_,
-apply_), plus build_addressing for the per-step addressing that page says both
-kernels read.
+apply_), plus build_addressing for the per-step addressing that, per that
+page's module overview, the shrink and the expand both take from the pool.
 """
 from __future__ import annotations
 
@@ -56,6 +56,7 @@ SIGNATURES = {
     "lora_apply_linear": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P, _P,
                                          _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "lora_apply_linear_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+    "lora_apply_linear_path": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P, _I32, _I32]),
 }
 
 
@@ -228,7 +229,9 @@ def _slices(out_slices: Sequence[int]):
 
 
 def expand_(h, b, addressing, ranks, scalings, y, out_slices: Sequence[int]) -> None:
-    """y[t, slice i] += scalings[slot(t)] * h[t, slice i] @ b[slot(t), slice i]^T."""
+    """Add each token's LoRA delta into y in place: for every fused output
+    slice i, the slot's scaling times the token's slice-i h columns (below
+    the slot's rank) against the slot's B rows of that slice."""
     order, indptr = _addr(addressing)
     ranks = _i32(ranks)
     dev = _dev(h, b, order, indptr, ranks, scalings, y)
@@ -246,6 +249,7 @@ def expand_(h, b, addressing, ranks, scalings, y, out_slices: Sequence[int]) -> 
 expand_fused = expand_
 
 _WS = {}
+_WS_RETIRED = []
 
 
 def workspace_bytes(T: int, in_features: int, slots: int, num_slices: int, R: int) -> int:
@@ -253,12 +257,23 @@ def workspace_bytes(T: int, in_features: int, slots: int, num_slices: int, R: in
 
 
 def _workspace(dev, nbytes: int):
-    """A zero-filled workspace cached per device; the library leaves its
-    counters at zero after every completed call, so it is reused as is."""
+    """The workspace lora_apply_linear gets when the caller passes none: one
+    zero-filled buffer per (device, stream), reused from call to call (every
+    completed call leaves the synchronisation counters at its start in a
+    state the next call accepts, so no clearing is needed).
+
+    A graph captured on a stream keeps the address of the workspace it was
+    captured with. When a later call needs a larger one, the old buffer is
+    kept alive (never freed while the process runs), so a graph that still
+    uses it stays valid. Calls that share one workspace must not run at the
+    same time: graphs captured on one stream and replayed concurrently on
+    other streams should each be given a workspace of their own."""
     import torch
     key = (str(dev), torch.cuda.current_stream(dev).cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _WS_RETIRED.append(ws)
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _WS[key] = ws
     return ws

@@ -1,7 +1,8 @@
 // Device-side slot addressing: token_slot -> (token_order, slot_indptr).
 //
-// Follows the mstar lora.backend page (module overview: both kernels read the
-// step's LoraAddressing, so eager and captured paths address slots alike).
+// Follows the mstar lora.backend page (module overview: the shrink and the
+// expand take their slot addressing from the pool's per-step addressing
+// object, so an eager step and a captured graph address slots the same way).
 // The grouping is a stable counting sort keyed by slot, dead tokens (slot
 // outside [0, slots)) keyed after every live slot. One workgroup of up to 16
 // waves does the whole batch, with no host round trip, so a serving step can

@@ -2,10 +2,11 @@
 // batch (fewer than 1024 tokens; larger batches run the segment-tiled
 // kernels), on bf16 MFMA.
 //
-// Follows the mstar lora.backend page, LoraBackend.apply_linear_ ("a backend
-// may fuse them"): the result is that of shrink (h = x @ A^T, per token's
-// slot) followed by expand (y += scaling * h @ B^T per fused slice), with h
-// kept in fp32 and never written to memory.
+// Follows the mstar lora.backend page, LoraBackend.apply_linear_ (the shrink
+// and the expand of one target, which a backend is free to run as one
+// kernel): the result is that of shrink (h = x @ A^T, per token's slot)
+// followed by expand (y += scaling * h @ B^T per fused slice), with h kept in
+// fp32.
 //
 // Work (one 512-thread workgroup per piece or item):
 //  * decode pieces, for segments of at most 16 tokens. A shrink piece

@@ -68,6 +68,25 @@ size_t partial_bytes(int32_t slots, int32_t S, int32_t R, int64_t in) {
 // segments of at most kLongSegment tokens (shrink, expand).
 constexpr int64_t kLargeBatch = 1024;
 
+// Whether lora_shrink's products run on the MFMA kernels (the shapes only
+// matter, not the output widths: a slice table of num_slices 16-wide slices
+// stands in for them).
+bool shrink_on_mfma(int dtype, int64_t T, int64_t in, int32_t S, int32_t R) {
+  SliceTable st;
+  st.n = S;
+  for (int i = 0; i <= S; ++i) st.off[i] = 16 * i;
+  return lora::sgmv_supported(dtype, st, R, (int)T, (int)in) &&
+         lora::fused_supported(dtype, st, R, (int)T, (int)in);
+}
+
+// Kernel family of lora_apply_linear for these shapes (LORA_PATH_*).
+int apply_path(int dtype, int64_t T, int64_t in, const SliceTable& st, int32_t R) {
+  if (!lora::fused_supported(dtype, st, R, (int)T, (int)in)) return LORA_PATH_VALU;
+  if (T < kLargeBatch) return LORA_PATH_FUSED;
+  return lora::sgmv_supported(dtype, st, R, (int)T, (int)in) ? LORA_PATH_SEGMENT
+                                                              : LORA_PATH_VALU;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,12 +190,7 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   // tiles, in a large batch every segment on the SGMV tiles, and the VALU
   // kernel writes only the zeros; otherwise (fp32, or sizes the MFMA kernels
   // do not take) the VALU kernel computes every segment.
-  SliceTable none;
-  none.n = 1;
-  none.off[0] = 0;
-  none.off[1] = 16;
-  const bool mfma = lora::sgmv_supported(dtype, none, R, (int)T, (int)in_features) &&
-                    lora::fused_supported(dtype, none, R, (int)T, (int)in_features);
+  const bool mfma = shrink_on_mfma(dtype, T, in_features, num_slices, R);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
                                      token_order, slot_indptr, ranks, h,
@@ -243,6 +257,17 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
   return hip_status(e);
 }
 
+int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int64_t* out_slices,
+                           int32_t num_slices, int32_t R) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return -LORA_ERR_UNSUPPORTED;
+  if (T < 0 || T > kMaxI32 || in_features < 1 || in_features > kMaxI32 || R < 1 || R > 256)
+    return -LORA_ERR_INVALID_ARG;
+  SliceTable tab;
+  const lora_status st = make_slices(dtype, out_slices, num_slices, R, &tab);
+  if (st != LORA_OK) return -st;
+  return apply_path(dtype, T, in_features, tab, R);
+}
+
 size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
                                          int32_t num_slices, int32_t R) {
   if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
@@ -278,16 +303,18 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
   float* h = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                       lora::counter_bytes(slots, num_slices) +
                                       partial_bytes(slots, num_slices, R, in_features));
-  if (lora::fused_supported(dtype, tab, R, (int)T, (int)in_features)) {
-    // The host picks the kernel family from T only (fixed per captured
-    // graph): small batches run everything in the fused kernel (decode
-    // pieces for segments of at most 16 tokens, 16-token prefill items for
-    // longer ones); larger batches run every segment through the SGMV
-    // shrink and expand, which write and read their h in the workspace.
-    // There the few-token segments are pure weight streaming, which the
-    // SGMV tiles' shared, deeper loads serve better than the decode pieces.
+  const int path = apply_path(dtype, T, in_features, tab, R);
+  if (path != LORA_PATH_VALU) {
+    // The host picks the kernel family from the shapes only (fixed per
+    // captured graph): small batches run everything in the fused kernel
+    // (decode pieces for segments of at most 16 tokens, 16-token prefill
+    // items for longer ones); larger batches run every segment through the
+    // SGMV shrink and expand, which write and read their h in the
+    // workspace. There the few-token segments are pure weight streaming,
+    // which the SGMV tiles' shared, deeper loads serve better than the
+    // decode pieces.
     hipError_t e;
-    if (T < kLargeBatch) {
+    if (path == LORA_PATH_FUSED) {
       e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
                                    token_order, slot_indptr, ranks, scalings, workspace, s);
     } else {

@@ -619,8 +619,11 @@ bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in) {
   if (dtype != kDtypeBF16 || R > 256) return false;
   const int64_t lim = (int64_t)1 << 31;
   const int64_t out = st.off[st.n];
+  // x, y, one slot's A and B, and h (read through a buffer resource by the
+  // expand) must each stay below 2 GiB
   if ((int64_t)T * in * 2 >= lim || (int64_t)T * out * 2 >= lim ||
-      (int64_t)out * R * 2 >= lim || (int64_t)R * in * 2 >= lim)
+      (int64_t)out * R * 2 >= lim || (int64_t)R * in * 2 >= lim ||
+      (int64_t)T * st.n * R * 4 >= lim)
     return false;
   for (int i = 0; i < st.n; ++i)
     if ((st.off[i + 1] - st.off[i]) % 16 != 0) return false;

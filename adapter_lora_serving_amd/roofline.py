@@ -64,8 +64,26 @@ def lora_call_cost(T: int, in_features: int, out_slices: Sequence[int], R: int, 
     return total, flops, terms
 
 
+def expert_row_slots(row_slot, expert_offsets, slots: int) -> np.ndarray:
+    """Pool entry of every row of an expert-sorted batch, for the byte model:
+    expert e owns rows [offsets[e], offsets[e+1]) and a row of slot s uses
+    entry e * slots + s; rows outside the expert ranges or with a slot outside
+    [0, slots) use none (-1)."""
+    rs = np.asarray(row_slot, dtype=np.int64)
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    r = np.arange(len(rs))
+    e = np.searchsorted(offs, r, side="right") - 1
+    live = (r >= offs[0]) & (r < offs[-1]) & (rs >= 0) & (rs < slots)
+    return np.where(live, e * slots + rs, -1)
+
+
 def workload_cost(wl, tg) -> Tuple[int, int, Dict[str, int]]:
-    """Cost of one target of a `workloads.Workload`."""
+    """Cost of one target of a `workloads.Workload` (an expert-sorted batch
+    takes each row's pool entry from its routing)."""
     e = 2 if wl.dtype == "bf16" else 4
+    ts = wl.token_slot
+    ex = getattr(wl, "experts", None)
+    if ts is None and ex is not None:
+        ts = expert_row_slots(ex["row_slot"], ex["offsets"], ex["slots"])
     return lora_call_cost(wl.T, tg.in_features, tg.out_slices, wl.R, wl.slots, wl.ranks,
-                          wl.token_slot, e, embedding=tg.embedding, ids=tg.ids)
+                          ts, e, embedding=tg.embedding, ids=tg.ids)

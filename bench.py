@@ -40,8 +40,13 @@ import workloads as W  # noqa: E402
 from adapter_lora_serving_amd.roofline import BF16_MFMA_PEAK_TFLOPS, HBM_PEAK_GBS, workload_cost  # noqa: E402
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["lora_common.h", "lora_kernels.h", "fused.hip", "sgmv.hip", "shrink.hip", "expand.hip",
-                  "lora_api.cpp"]
+CSRC = os.path.join(ROOT, "adapter_lora_serving_amd", "csrc")
+
+
+def kernel_sources():
+    """Every device and launch source of the library (all of csrc/)."""
+    return sorted(n for n in os.listdir(CSRC)
+                  if n.endswith((".hip", ".h", ".cpp")))
 
 
 def eprint(*a):
@@ -53,9 +58,8 @@ def kernel_source_hash() -> str:
     removed, so that a comment edit does not invalidate recorded counters."""
     import re
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "adapter_lora_serving_amd", "csrc")
-    for name in KERNEL_SOURCES:
-        p = os.path.join(csrc, name)
+    for name in kernel_sources():
+        p = os.path.join(CSRC, name)
         if os.path.exists(p):
             text = open(p, encoding="utf-8").read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -81,17 +85,46 @@ def measured_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, tg, budget_s: float):
-    """The fp64 CPU oracle as it stands, on the same batch, for ~budget_s."""
-    import oracle as O
-    threads = os.cpu_count() or 1
+def host_info():
+    """CPU model, the CPUs this process may run on, and the BLAS build the
+    oracle's matrix products use (threads, library, version)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    blas = {}
     try:
         from threadpoolctl import threadpool_info
         info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         if info:
-            threads = max(int(i.get("num_threads", 1)) for i in info)
+            i = max(info, key=lambda d: int(d.get("num_threads", 1)))
+            blas = {"library": i.get("internal_api"), "version": i.get("version"),
+                    "threads": int(i.get("num_threads", 1)),
+                    "threading": i.get("threading_layer"),
+                    "arch": i.get("architecture")}
     except Exception:
         pass
+    return model, affinity, blas
+
+
+def cpu_baseline(wl, tg, budget_s: float):
+    """The fp64 CPU oracle as it stands, on the same batch, for ~budget_s."""
+    import oracle as O
+    model, affinity, blas = host_info()
+    threads = blas.get("threads", affinity)
+    ex = getattr(wl, "experts", None)
+    if wl.token_slot is None and ex is not None:
+        # rows of an expert-sorted batch: the oracle's own key of each row
+        wl = W.with_token_slot(wl, O.expert_keys(ex["row_slot"], ex["offsets"], ex["experts"],
+                                                 ex["slots"]))
     runs = 0
     t0 = time.perf_counter()
     while True:
@@ -103,7 +136,8 @@ def cpu_baseline(wl, tg, budget_s: float):
     return {"value": round(wl.T * runs / el, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"the full {wl.T}-token batch of the same workload, {runs} oracle runs "
-                      f"(fp64 NumPy, bf16 decode included) in {el:.1f} s"}
+                      f"(fp64 NumPy, bf16 decode included) in {el:.1f} s",
+            "cpu_model": model, "affinity_cpus": int(affinity), "blas": blas}
 
 
 def main():
@@ -120,7 +154,8 @@ def main():
                          "folded onto 64 routing logits, decode batch); tp8_qkv_decode, "
                          "tp8_prefill (one GPU's share of a TP=8 projection; --target "
                          "gate_up or down for the latter); moe_experts (the routed-expert "
-                         "LoRA on 512 expert-sorted rows, its addressing by (expert, slot))")
+                         "LoRA on 512 expert-sorted rows, its addressing by (expert, slot); "
+                         "--target expert_gate_up or expert_down)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -165,7 +200,8 @@ def main():
 
     ranks = torch.from_numpy(wl.ranks).to(dev)
     scal = torch.from_numpy(wl.scalings).to(dev)
-    ts_host = torch.from_numpy(wl.token_slot.astype(np.int32))
+    ts_host = (None if wl.token_slot is None
+               else torch.from_numpy(wl.token_slot.astype(np.int32)))
     sets = []
     if tg.embedding:
         x0 = torch.from_numpy(tg.ids.astype(np.int32)).to(dev)
@@ -181,7 +217,8 @@ def main():
         return L.build_addressing_experts(s["rs"], s["offs"], ex["experts"], ex["slots"], out=out)
 
     for i in range(n_sets):
-        s = dict(x=x0.clone(), a=a0.clone(), b=b0.clone(), y=y0.clone(), ts=ts_host.to(dev))
+        s = dict(x=x0.clone(), a=a0.clone(), b=b0.clone(), y=y0.clone(),
+                 ts=None if ts_host is None else ts_host.to(dev))
         if ex is not None:
             s["rs"] = torch.from_numpy(ex["row_slot"]).to(dev)
             s["offs"] = torch.from_numpy(ex["offsets"]).to(dev)

@@ -85,10 +85,11 @@ const char* lora_version(void);
 /*
  * lora_build_addressing: group the batch's tokens by adapter slot.
  *
- * Source: lora.backend module overview (both kernels read the step's
- * LoraAddressing, never a model-side index, so eager and captured paths
- * address slots alike) and shrink_reference / expand_reference_, which take
- * token_order and slot_indptr.
+ * Source: lora.backend module overview (the shrink and the expand take
+ * their slot addressing from the adapter pool's per-step addressing object,
+ * not from an index the model keeps, which is what lets an eager step and a
+ * captured graph address slots the same way) and shrink_reference /
+ * expand_reference_, which take token_order and slot_indptr.
  *
  * Output: token_order is a permutation of [0, T). For each slot s the
  * segment token_order[slot_indptr[s] .. slot_indptr[s+1]) holds the tokens
@@ -217,8 +218,9 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
 /*
  * lora_apply_linear: shrink then expand into y for a linear target.
  *
- * Source: lora.backend, LoraBackend.apply_linear_ ("a backend may fuse
- * them"). Same result as lora_shrink followed by lora_expand (h kept in
+ * Source: lora.backend, LoraBackend.apply_linear_ (the shrink and the
+ * expand of one linear target, which a backend is free to run as one
+ * kernel). Same result as lora_shrink followed by lora_expand (h kept in
  * float32 inside the workspace, never rounded). workspace must be at least
  * lora_apply_linear_workspace_bytes(...) bytes, 256-byte aligned, and zero-
  * filled before its FIRST use. Its first 4 MiB hold synchronisation
@@ -239,6 +241,21 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T,
 /* Workspace bytes lora_apply_linear needs for these sizes (0 on bad input). */
 size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t slots,
                                          int32_t num_slices, int32_t R);
+
+/*
+ * lora_apply_linear_path: which kernel family lora_apply_linear runs for
+ * these shapes (host-only query; touches no device memory).
+ * Returns LORA_PATH_FUSED (the one-launch fused kernel of a small bf16
+ * batch), LORA_PATH_SEGMENT (the MFMA segment-tiled shrink and expand of a
+ * large bf16 batch, h in the workspace) or LORA_PATH_VALU (the vector
+ * kernels: fp32, or sizes whose buffers the MFMA kernels' 32-bit offsets
+ * cannot reach: x, y, h or one slot's A or B of 2 GiB or more), or a
+ * negated lora_status for bad arguments. out_slices (host) as in
+ * lora_apply_linear.
+ */
+enum { LORA_PATH_VALU = 0, LORA_PATH_FUSED = 1, LORA_PATH_SEGMENT = 2 };
+int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int64_t* out_slices,
+                           int32_t num_slices, int32_t R);
 
 #ifdef __cplusplus
 }

@@ -75,8 +75,9 @@ def _live(slot: int, slots: int) -> bool:
 
 # ---------------------------------------------------------------------------
 # addressing: token_order / slot_indptr
-# (lora.backend, module overview: "Both read the step's LoraAddressing";
-#  shrink_reference / expand_reference_ take token_order and slot_indptr)
+# (lora.backend, module overview: the shrink and the expand both take the
+#  per-step addressing from the adapter pool; shrink_reference and
+#  expand_reference_ take token_order and slot_indptr)
 # ---------------------------------------------------------------------------
 
 def build_addressing(token_slot: Sequence[int], slots: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -196,20 +197,16 @@ def expand(y0: np.ndarray, h: np.ndarray, b: np.ndarray, token_slot: np.ndarray,
     return y
 
 
-def apply_linear(x, y0, a, b, token_slot, ranks, scalings, out_slices, R):
-    """Shrink then expand for a linear target (lora.backend, apply_linear_)."""
-    h = shrink(x, a, token_slot, ranks, len(out_slices), R)
-    return expand(y0, h, b, token_slot, ranks, scalings, out_slices, R)
+def base_projection(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """The base layer's own output, y[t, o] = sum_c x[t, c] * w[o, c]: one
+    product over the fused weight, whose shards (q, k, v or gate, up) are
+    stacked along the output dimension in order (mstar.model.components.linear,
+    FusedColumnLinear.forward). The LoRA delta is then added on top of it
+    (expand, with this as y0), as when the expand runs inside the base
+    projection's epilogue.
 
-
-def apply(inp, y0, a, b, token_slot, ranks, scalings, out_slices, R, embedding=False):
-    """Gather (embedding target, `inp` are ids) or shrink, then expand
-    (lora.backend, LoraBackend.apply_)."""
-    if embedding:
-        h = gather_shrink(inp, a, token_slot, ranks, R)
-    else:
-        h = shrink(inp, a, token_slot, ranks, len(out_slices), R)
-    return expand(y0, h, b, token_slot, ranks, scalings, out_slices, R)
+    x: float64 [T, in]; w: float64 [out, in]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
 
 
 # ---------------------------------------------------------------------------

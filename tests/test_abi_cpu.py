@@ -156,3 +156,30 @@ def test_binding_refuses_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     with pytest.raises(L.LoraError):
         L.build_addressing(torch.zeros(4, dtype=torch.int32), 2)
+
+
+def test_apply_linear_path_predicate(lib):
+    """The kernel family lora_apply_linear picks for a shape, queried on the
+    host: fused for a small bf16 batch, the segment tiles for a large one,
+    the vector kernels for fp32 and wherever a buffer the MFMA kernels read
+    through 32-bit offsets (x, y, h, one slot's A or B) reaches 2 GiB."""
+    VALU, FUSED, SEGMENT = 0, 1, 2
+    f = lib.lora_apply_linear_path
+    qkv = _slices(4096, 1024, 1024)
+    assert f(1, 256, 4096, qkv, 3, 16) == FUSED
+    assert f(1, 8192, 4096, _slices(14336, 14336), 2, 64) == SEGMENT
+    assert f(0, 256, 4096, qkv, 3, 16) == VALU                    # fp32
+    # h = T * S * R * 4 bytes: 2^21 tokens at R = 128 hold 1 GiB, at R = 256 2 GiB
+    T = 1 << 21
+    assert f(1, T, 8, _slices(16), 1, 128) == SEGMENT
+    assert f(1, T, 8, _slices(16), 1, 256) == VALU
+    assert f(1, T // 2, 8, _slices(16, 16), 2, 256) == VALU      # two slices of h
+    assert f(1, T // 2, 8, _slices(16), 1, 256) == SEGMENT
+    # y of 2 GiB (T * out * 2) and x of 2 GiB (T * in * 2)
+    assert f(1, 1 << 16, 8, _slices(1 << 14), 1, 16) == VALU
+    assert f(1, 1 << 16, 1 << 14, _slices(16), 1, 16) == VALU
+    # bad arguments come back as a negated status
+    assert f(7, 256, 4096, qkv, 3, 16) == -UNSUPPORTED
+    assert f(1, -1, 4096, qkv, 3, 16) == -INVALID
+    assert f(1, 256, 4096, qkv, 9, 16) == -UNSUPPORTED
+    assert f(1, 256, 4096, _slices(12), 1, 16) == -ALIGN

@@ -357,22 +357,267 @@ def test_pins_catch_planted_mistake(mut):
     assert caught, f"no pin catches mutant {mut}"
 
 
-def test_expert_addressing_is_lexicographic_sort():
-    """The expert addressing equals a plain stable sort of the rows by
-    (expert, slot), dead rows last: checked against Python's sorted."""
+# ---------------------------------------------------------------------------
+# the routed-expert addressing (page "spark_model/lora/expert_apply.rs", the
+# experts injection shape): composite key of (expert, slot) per row of an
+# expert-sorted batch, then the stable grouping of the addressing
+# ---------------------------------------------------------------------------
+
+GOLD_EXPERT = os.path.join(os.path.dirname(__file__), "golden", "expert_keys.json")
+
+
+def _experts_addressing(impl, row_slot, offs, E, slots):
+    return impl.build_addressing(impl.expert_keys(row_slot, offs, E, slots), E * slots)
+
+
+def check_expert_keys_golden(impl):
+    """The hand-worked example: rows before expert_offsets[0] and at or after
+    expert_offsets[E], an empty expert, and slots outside [0, slots)."""
+    g = json.load(open(GOLD_EXPERT))
+    keys = impl.expert_keys(g["row_slot"], g["expert_offsets"], g["num_experts"], g["slots"])
+    assert np.asarray(keys).tolist() == g["expect_keys"]
+    order, indptr = _experts_addressing(impl, g["row_slot"], g["expert_offsets"],
+                                        g["num_experts"], g["slots"])
+    assert order.tolist() == g["expect_token_order"]
+    assert indptr.tolist() == g["expect_slot_indptr"]
+
+
+def check_expert_vs_sorted(impl):
+    """Brute force: Python's sorted by (expert, slot, row), dead rows (bad slot,
+    or outside [offsets[0], offsets[E])) last by row; expert bounds drawn so
+    that rows fall outside them at both ends."""
     rng = np.random.default_rng(11)
-    for rows, E, slots in ((1, 1, 1), (40, 3, 5), (300, 8, 16)):
-        cuts = np.sort(rng.integers(0, rows + 1, size=E - 1))
-        offs = np.concatenate([[0], cuts, [rows]]).astype(np.int32)
+    for rows, E, slots in ((1, 1, 1), (40, 3, 5), (300, 8, 16), (97, 5, 3)):
+        cuts = np.sort(rng.integers(0, rows + 1, size=E + 1))
+        offs = cuts.astype(np.int32)                 # offs[0] > 0 and offs[E] < rows mostly
+        if rows > 4:
+            offs[0], offs[-1] = min(offs[0], 2) + 1, max(offs[-1], rows - 3) - 1
+            offs = np.maximum.accumulate(offs)
         row_slot = rng.integers(-1, slots + 1, size=rows)
-        order, indptr = O.build_addressing_experts(row_slot, offs, E, slots)
-        expert = np.searchsorted(offs, np.arange(rows), side="right") - 1
-        live = (row_slot >= 0) & (row_slot < slots)
-        want = sorted(range(rows), key=lambda r: (0, expert[r], row_slot[r], r) if live[r]
+        order, indptr = _experts_addressing(impl, row_slot, offs, E, slots)
+        expert = [next((e for e in range(E) if offs[e] <= r < offs[e + 1]), None)
+                  for r in range(rows)]
+        live = [expert[r] is not None and 0 <= row_slot[r] < slots for r in range(rows)]
+        want = sorted(range(rows), key=lambda r: (0, expert[r], int(row_slot[r]), r) if live[r]
                       else (1, 0, 0, r))
         assert order.tolist() == want
         for e in range(E):
             for sl in range(slots):
                 k = e * slots + sl
-                seg = order[indptr[k]:indptr[k + 1]]
-                assert all(expert[r] == e and row_slot[r] == sl for r in seg)
+                assert int(indptr[k + 1] - indptr[k]) == sum(
+                    1 for r in range(rows) if live[r] and expert[r] == e and row_slot[r] == sl)
+        assert int(indptr[-1]) == sum(live)
+
+
+EXPERT_PINS = [check_expert_keys_golden, check_expert_vs_sorted]
+
+
+@pytest.mark.parametrize("pin", EXPERT_PINS, ids=[f.__name__ for f in EXPERT_PINS])
+def test_expert_pin(pin):
+    pin(O)
+
+
+EXPERT_MUTANTS = [
+    # rows outside every expert range default to expert 0 instead of dead
+    ("expert_keys", "keys = np.full(len(row_slot), -1, dtype=np.int64)",
+     "keys = np.where((np.asarray(row_slot) >= 0) & (np.asarray(row_slot) < slots), "
+     "np.asarray(row_slot), -1).astype(np.int64)"),
+    # an expert's range taken as closed at its end
+    ("expert_keys", "int(expert_offsets[e + 1])", "int(expert_offsets[e + 1]) + 1"),
+    # expert and slot transposed in the key
+    ("expert_keys", "keys[r] = e * slots + int(row_slot[r])",
+     "keys[r] = int(row_slot[r]) * num_experts + e"),
+    # a bad slot not treated as dead
+    ("expert_keys", "_live(int(row_slot[r]), slots)", "int(row_slot[r]) < slots"),
+]
+
+
+def _expert_mutant(fn_name, old, new):
+    src = inspect.getsource(getattr(O, fn_name))
+    assert old in src, (fn_name, old)
+    ns = dict(vars(O))
+    exec(src.replace(old, new, 1), ns)
+    return types.SimpleNamespace(expert_keys=ns["expert_keys"],
+                                 build_addressing=O.build_addressing)
+
+
+@pytest.mark.parametrize("mut", EXPERT_MUTANTS, ids=[f"{m[0]}:{m[2][:28]}" for m in EXPERT_MUTANTS])
+def test_expert_pins_catch_planted_mistake(mut):
+    impl = _expert_mutant(*mut)
+    caught = []
+    for pin in EXPERT_PINS:
+        try:
+            pin(impl)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {mut}"
+
+
+# ---------------------------------------------------------------------------
+# the workload-level helpers every GPU parity test goes through
+# ---------------------------------------------------------------------------
+
+def _worked_example_workload():
+    """The hand-worked linear example as a generated workload (float32: every
+    value in it is exact in fp32)."""
+    g = json.load(open(GOLD))
+    L = g["linear"]
+    f32 = lambda v: np.asarray(v, dtype=np.float32)  # noqa: E731
+    wl = W.Workload(name="worked", dtype="f32", T=len(L["token_slot"]), R=L["R"],
+                    slots=L["slots"], ranks=np.asarray(L["ranks"], np.int32),
+                    scalings=f32(L["scalings"]), token_slot=np.asarray(L["token_slot"], np.int32))
+    wl.targets.append(W.Target(name="t", in_features=len(L["x"][0]),
+                               out_slices=tuple(L["out_slices"]), a=f32(L["a"]), b=f32(L["b"]),
+                               y0=f32(L["y0"]), x=f32(L["x"])))
+    E = g["embedding"]
+    we = W.Workload(name="worked_emb", dtype="f32", T=len(E["token_slot"]), R=E["R"],
+                    slots=E["slots"], ranks=np.asarray(E["ranks"], np.int32),
+                    scalings=np.ones(E["slots"], np.float32),
+                    token_slot=np.asarray(E["token_slot"], np.int32))
+    a = f32(E["a"])
+    we.targets.append(W.Target(name="e", in_features=a.shape[2], out_slices=(1,), a=a,
+                               b=np.ones((E["slots"], 1, E["R"]), np.float32),
+                               y0=np.zeros((len(E["token_slot"]), 1), np.float32),
+                               ids=np.asarray(E["ids"], np.int32)))
+    return g, wl, we
+
+
+def check_run_target_worked_example(impl):
+    """run_target (decode, shrink or gather, then expand) reproduces the
+    hand-worked h and y; the embedding target's y is the sum of its h row
+    (b = 1, scaling 1, y0 = 0)."""
+    g, wl, we = _worked_example_workload()
+    h, y = impl.run_target(wl, wl.targets[0])
+    assert np.array_equal(h, np.array(g["linear"]["expect_h"], float))
+    assert np.array_equal(y, np.array(g["linear"]["expect_y"], float))
+    he, ye = impl.run_target(we, we.targets[0])
+    want = np.array(g["embedding"]["expect_h"], float)
+    assert np.array_equal(he, want)
+    assert np.array_equal(ye[:, 0], want.sum(axis=1))
+
+
+def check_run_target_decodes_bf16(impl):
+    """The bf16 path of run_target decodes the bit patterns exactly: the same
+    example written as bf16 bits (all its values are exact in bf16) gives the
+    same h and y."""
+    g, wl, _ = _worked_example_workload()
+    tg = wl.targets[0]
+    bits = {k: W.f32_to_bf16_bits(getattr(tg, k)) for k in ("a", "b", "y0", "x")}
+    wb = W.Workload(**{**wl.__dict__, "dtype": "bf16", "targets": []})
+    wb.targets.append(W.Target(**{**tg.__dict__, **bits}))
+    h, y = impl.run_target(wb, wb.targets[0])
+    assert np.array_equal(h, np.array(g["linear"]["expect_h"], float))
+    assert np.array_equal(y, np.array(g["linear"]["expect_y"], float))
+
+
+def check_within_tolerance(impl):
+    O = impl  # noqa: N806  (the checks below read as calls of the oracle)
+    ref = np.array([0.0, 1.0, -2.0, 100.0])
+    # just inside the bound 1e-2 + 1e-2 |ref| passes, just past it fails
+    bound = 1e-2 + 1e-2 * np.abs(ref)
+    ok, worst = O.within_tolerance(ref + 0.999 * bound, ref)
+    assert ok and abs(worst - 0.999) < 1e-9
+    ok, worst = O.within_tolerance(ref - 0.999 * bound, ref)
+    assert ok and abs(worst - 0.999) < 1e-9
+    ok, worst = O.within_tolerance(ref + 1.001 * bound, ref)
+    assert not ok and worst > 1.0
+    ok, worst = O.within_tolerance(ref - 1.001 * bound, ref)
+    assert not ok and worst > 1.0
+    # a single element past the bound fails; the worst ratio names it
+    gpu = ref.copy()
+    gpu[3] += 3.0 * bound[3]
+    ok, worst = O.within_tolerance(gpu, ref)
+    assert not ok and abs(worst - 3.0) < 1e-9
+    # NaN or inf in the result never passes
+    for bad in (np.nan, np.inf, -np.inf):
+        gpu = ref.copy()
+        gpu[1] = bad
+        assert not O.within_tolerance(gpu, ref)[0]
+    # tighter bounds are honoured
+    assert O.within_tolerance(ref + 5e-6, ref, atol=1e-5, rtol=1e-5)[0]
+    assert not O.within_tolerance(ref + 5e-4, ref, atol=1e-5, rtol=1e-5)[0]
+    # empty input passes trivially
+    assert O.within_tolerance(np.zeros(0), np.zeros(0)) == (True, 0.0)
+
+
+HELPER_PINS = [check_run_target_worked_example, check_run_target_decodes_bf16,
+               check_within_tolerance]
+
+
+@pytest.mark.parametrize("pin", HELPER_PINS, ids=[f.__name__ for f in HELPER_PINS])
+def test_helper_pin(pin):
+    pin(O)
+
+
+HELPER_MUTANTS = [
+    ("run_target", "y0 = decode(tg.y0, wl.dtype)", "y0 = 0.0 * decode(tg.y0, wl.dtype)"),
+    ("run_target", "tg.num_slices, wl.R)", "1, wl.R)"),
+    ("run_target", "wl.scalings, tg.out_slices", "np.ones_like(wl.scalings), tg.out_slices"),
+    ("run_target", "b = decode(tg.b, wl.dtype)", "b = decode(tg.b, \"f32\")"),
+    ("within_tolerance", "np.abs(gpu - ref)", "(gpu - ref)"),
+    ("within_tolerance", "rtol * np.abs(ref)", "rtol * np.abs(gpu)"),
+    ("within_tolerance", "ratio <= 1.0", "ratio <= 1.5"),
+    ("within_tolerance", "np.nanmax(ratio)", "np.nanmean(ratio)"),
+]
+
+
+@pytest.mark.parametrize("mut", HELPER_MUTANTS, ids=[f"{m[0]}:{m[2][:28]}" for m in HELPER_MUTANTS])
+def test_helper_pins_catch_planted_mistake(mut):
+    fn_name, old, new = mut
+    src = inspect.getsource(getattr(O, fn_name))
+    assert old in src, mut
+    ns = dict(vars(O))
+    exec(src.replace(old, new, 1), ns)
+    impl = types.SimpleNamespace(run_target=O.run_target, within_tolerance=O.within_tolerance)
+    setattr(impl, fn_name, ns[fn_name])
+    caught = []
+    for pin in HELPER_PINS:
+        try:
+            pin(impl)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {mut}"
+
+
+# ---------------------------------------------------------------------------
+# the base projection (mstar.model.components.linear, FusedColumnLinear) and
+# the delta added on top of it: the merged-weight closed form
+# ---------------------------------------------------------------------------
+
+def test_base_projection_brute_force_and_identity():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, 7))
+    w = rng.standard_normal((6, 7))
+    y = O.base_projection(x, w)
+    for t in range(5):
+        for o in range(6):
+            assert abs(y[t, o] - sum(x[t, c] * w[o, c] for c in range(7))) < 1e-12
+    assert np.array_equal(O.base_projection(x, np.eye(7)), x)
+    # shards stacked along the output dimension give their columns in order
+    wq, wk = rng.standard_normal((4, 7)), rng.standard_normal((2, 7))
+    yq, yk = O.base_projection(x, wq), O.base_projection(x, wk)
+    assert np.array_equal(O.base_projection(x, np.vstack([wq, wk])), np.hstack([yq, yk]))
+
+
+def test_base_plus_delta_is_merged_weight():
+    """For one slot at full rank, the base projection plus the LoRA delta is
+    the projection through the merged weight W_i + s * B_i @ A_i per slice
+    (the closed form of a LoRA-adapted linear layer)."""
+    rng = np.random.default_rng(22)
+    T, in_f, R, out_slices = 9, 13, 3, (5, 4, 6)
+    S = len(out_slices)
+    out = sum(out_slices)
+    x = rng.standard_normal((T, in_f))
+    w = rng.standard_normal((out, in_f))
+    a = rng.standard_normal((1, S * R, in_f))
+    b = rng.standard_normal((1, out, R))
+    s = 0.75
+    ts = np.zeros(T, int)
+    h = O.shrink(x, a, ts, np.array([R]), S, R)
+    y = O.expand(O.base_projection(x, w), h, b, ts, np.array([R]), np.array([s]), out_slices, R)
+    merged = w.copy()
+    off = 0
+    for i, wd in enumerate(out_slices):
+        merged[off:off + wd] += s * b[0, off:off + wd] @ a[0, i * R:(i + 1) * R]
+        off += wd
+    np.testing.assert_allclose(y, x @ merged.T, rtol=1e-12, atol=1e-12)

@@ -26,7 +26,7 @@ BF16_NAN = np.uint16(0x7FC0)
 __all__ = [
     "Target", "Workload", "f32_to_bf16_bits", "make_workload", "make_config",
     "CONFIG_NAMES", "poison_unread", "zipf_request_lengths", "permute_tokens",
-    "take_tokens",
+    "take_tokens", "with_token_slot", "make_moe_experts", "make_router_fold", "make_tp_share",
 ]
 
 
@@ -80,7 +80,7 @@ class Workload:
     slots: int
     ranks: np.ndarray           # int32 [slots]
     scalings: np.ndarray        # float32 [slots]
-    token_slot: np.ndarray      # int32 [T]; outside [0, slots) means "no adapter"
+    token_slot: Optional[np.ndarray]  # int32 [T]; outside [0, slots) means "no adapter"
     targets: List[Target] = field(default_factory=list)
     seed: int = 0
 
@@ -200,17 +200,27 @@ MOE_EXPERTS = "moe_experts_bf16"
 def make_moe_experts(seed: int = 0, *, T: int = 256, experts: int = 8, topk: int = 2,
                      hidden: int = 4096, inter: int = 14336, slots: int = 32,
                      y0_zero: bool = False) -> Workload:
-    """The routed-expert LoRA delta on the rows of an expert-sorted grouped
-    GEMM: each token goes to `topk` distinct experts drawn uniformly, the
-    rows (token, expert) are sorted by expert (stably, by token), and each
-    row carries its token's slot. The delta of a row uses the LoRA of
-    (expert, slot); as a linear target that is virtual slot k = expert *
-    slots + slot over experts * slots slots (A, B, ranks and scalings indexed
-    by k; a slot's rank and scaling are the same for every expert). The
-    pages give no sizes: an 8-expert, top-2 MoE with 4096 hidden and 14336
-    intermediate (the expert gate/up projection), over the decode recipe's
-    256 tokens and 32 slots. `wl.experts` holds what the device addressing
-    takes: the base slots, row_slot and expert_offsets."""
+    """The routed-expert LoRA on the rows of an expert-sorted grouped GEMM.
+
+    Routing: each of T tokens goes to `topk` distinct experts drawn uniformly;
+    the (token, expert) rows are laid out sorted by expert (stably, by
+    token), as the base grouped GEMM holds them, and every row carries its
+    token's adapter slot. `wl.experts` holds that routing: row_slot [rows],
+    expert_offsets [experts + 1] (expert e owns rows [offsets[e],
+    offsets[e+1])), and the number of experts and of base slots.
+
+    Adapter pool: one LoRA per (expert, slot), stored at pool index
+    expert * slots + slot (experts * slots entries: A, B, ranks, scalings);
+    a slot's rank and scaling are the same for every expert. Which pool entry
+    a row uses is left to the method (its addressing); `wl.token_slot` is
+    None here.
+
+    Targets: the expert gate/up projection (in = hidden, out slices (inter,
+    inter)), whose delta goes in before the activation, and the expert down
+    projection (in = inter, out = hidden), whose delta goes in after the down
+    product. The pages give no sizes: an 8-expert, top-2 MoE with 4096
+    hidden and 14336 intermediate, over the decode recipe's 256 tokens and 32
+    slots (ranks 8 or 16, scaling 2)."""
     rng = np.random.default_rng(seed)
     base_ranks = rng.choice(np.array([8, 16]), size=slots)
     tok_slot = rng.integers(0, slots, size=T, dtype=np.int64)
@@ -221,16 +231,30 @@ def make_moe_experts(seed: int = 0, *, T: int = 256, experts: int = 8, topk: int
     tok, ex = tok[order], ex[order]
     offsets = np.concatenate([[0], np.cumsum(np.bincount(ex, minlength=experts))])
     row_slot = tok_slot[tok]
-    keys = ex * slots + row_slot
+    rows = len(row_slot)
     vslots = experts * slots
-    wl = make_workload(name=MOE_EXPERTS, dtype="bf16", T=len(keys), in_features=hidden,
-                       out_slices=(inter, inter), R=16, slots=vslots,
-                       ranks=np.tile(base_ranks, experts),
-                       scalings=np.full(vslots, 2.0, np.float32), token_slot=keys, seed=seed,
-                       rng=rng, y0_zero=y0_zero, target_name="expert_gate_up")
+    R = 16
+    wl = Workload(name=MOE_EXPERTS, dtype="bf16", T=rows, R=R, slots=vslots,
+                  ranks=np.tile(base_ranks, experts).astype(np.int32),
+                  scalings=np.full(vslots, 2.0, np.float32), token_slot=None, seed=seed)
+    wl.targets.append(_draw_target(rng, "expert_gate_up", "bf16", rows, hidden, (inter, inter),
+                                   R, vslots, y0_zero=y0_zero))
+    wl.targets.append(_draw_target(rng, "expert_down", "bf16", rows, inter, (hidden,), R,
+                                   vslots, y0_zero=y0_zero))
     wl.experts = dict(experts=experts, slots=slots, row_slot=row_slot.astype(np.int32),
                       offsets=offsets.astype(np.int32))
     return wl
+
+
+def with_token_slot(wl: Workload, token_slot: np.ndarray) -> Workload:
+    """The same workload with the given per-token slot array (for instance the
+    pool index of every row of an expert-sorted batch, which the method's
+    own addressing gives)."""
+    out = Workload(**{**wl.__dict__, "targets": list(wl.targets),
+                      "token_slot": np.asarray(token_slot, dtype=np.int32)})
+    if hasattr(wl, "experts"):
+        out.experts = wl.experts
+    return out
 
 
 TP_SHARES = ("tp8_qkv_decode", "tp8_prefill")
