@@ -621,3 +621,21 @@ def test_base_plus_delta_is_merged_weight():
         merged[off:off + wd] += s * b[0, off:off + wd] @ a[0, i * R:(i + 1) * R]
         off += wd
     np.testing.assert_allclose(y, x @ merged.T, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_workload_through_the_oracle():
+    """The routed-expert workload carries routing and pool only; with each
+    row's pool entry from oracle.expert_keys it runs through the oracle, and
+    every live row's entry is (its expert, its token's slot)."""
+    wl = W.make_moe_experts(3, T=24, experts=4, hidden=32, inter=48, slots=5)
+    assert wl.token_slot is None
+    e = wl.experts
+    keys = O.expert_keys(e["row_slot"], e["offsets"], e["experts"], e["slots"])
+    kw = W.with_token_slot(wl, keys)
+    assert kw.experts is e and kw.slots == 4 * 5 and kw.T == 48
+    expert = np.searchsorted(e["offsets"], np.arange(kw.T), side="right") - 1
+    assert np.array_equal(keys, expert * 5 + e["row_slot"])
+    for name in ("expert_gate_up", "expert_down"):
+        tg = kw.target(name)
+        h, y = O.run_target(kw, tg)
+        assert np.all(np.isfinite(y)) and y.shape == (48, tg.out_features)

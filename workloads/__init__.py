@@ -16,6 +16,7 @@ token->slot, ids, then per target x, A, B, y0.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
 
@@ -250,8 +251,8 @@ def with_token_slot(wl: Workload, token_slot: np.ndarray) -> Workload:
     """The same workload with the given per-token slot array (for instance the
     pool index of every row of an expert-sorted batch, which the method's
     own addressing gives)."""
-    out = Workload(**{**wl.__dict__, "targets": list(wl.targets),
-                      "token_slot": np.asarray(token_slot, dtype=np.int32)})
+    out = dataclasses.replace(wl, targets=list(wl.targets),
+                              token_slot=np.asarray(token_slot, dtype=np.int32))
     if hasattr(wl, "experts"):
         out.experts = wl.experts
     return out
