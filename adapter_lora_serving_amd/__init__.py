@@ -29,7 +29,7 @@ _LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
 _LIB = None
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "alignment", 4: "workspace",
-          5: "HIP launch failed"}
+          5: "HIP launch failed", 6: "scratch limit"}
 
 Addressing = namedtuple("Addressing", ["token_order", "slot_indptr"])
 
@@ -57,6 +57,9 @@ SIGNATURES = {
                                          _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "lora_apply_linear_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "lora_apply_linear_path": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P, _I32, _I32]),
+    "lora_apply_linear_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P,
+                                                 _P, _I32, _I32, _P, _P, _P, _P, _P]),
+    "lora_noalloc_scratch_bytes": (_SZ, []),
 }
 
 

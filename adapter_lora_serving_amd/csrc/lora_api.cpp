@@ -99,6 +99,8 @@ const char* lora_status_string(int status) {
     case LORA_ERR_ALIGNMENT: return "pointer or row width not 16-byte aligned";
     case LORA_ERR_WORKSPACE: return "workspace missing or too small";
     case LORA_ERR_HIP: return "HIP launch failed";
+    case LORA_ERR_SCRATCH_LIMIT:
+      return "sizes need more than the static scratch array of lora_apply_linear_noalloc";
     default: return "unknown status";
   }
 }

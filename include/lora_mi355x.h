@@ -71,7 +71,9 @@ typedef enum lora_status {
   LORA_ERR_UNSUPPORTED = 2, /* dtype, R, num_slices or slots outside the supported set */
   LORA_ERR_ALIGNMENT = 3,   /* a pointer or a row width breaks the 16-byte rule above */
   LORA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
-  LORA_ERR_HIP = 5          /* a kernel launch failed (hipGetLastError after launch) */
+  LORA_ERR_HIP = 5,         /* a kernel launch failed (hipGetLastError after launch) */
+  LORA_ERR_SCRATCH_LIMIT = 6 /* the sizes need more than the static scratch array of
+                                lora_apply_linear_noalloc holds */
 } lora_status;
 
 typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
@@ -256,6 +258,36 @@ size_t lora_apply_linear_workspace_bytes(int64_t T, int64_t in_features, int32_t
 enum { LORA_PATH_VALU = 0, LORA_PATH_FUSED = 1, LORA_PATH_SEGMENT = 2 };
 int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int64_t* out_slices,
                            int32_t num_slices, int32_t R);
+
+/*
+ * lora_apply_linear_noalloc: lora_apply_linear without a workspace argument,
+ * for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid the allocator).
+ *
+ * Same arguments, semantics, result and kernels as lora_apply_linear, minus
+ * workspace / workspace_bytes: the workspace is a static device array of
+ * LORA_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on every GPU it
+ * runs on until the process ends. The call allocates nothing (no hipMalloc,
+ * no allocating library routine); the first call on a device looks the
+ * array's address up once (hipGetSymbolAddress), so make that first call
+ * outside graph capture where possible.
+ * Sizes whose lora_apply_linear_workspace_bytes(...) exceed the array are
+ * refused with LORA_ERR_SCRATCH_LIMIT before anything else is done.
+ * stream must belong to the current device (else LORA_ERR_INVALID_ARG).
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU race and must not be issued. The array keeps the last call's
+ * contents; nothing in it needs clearing between calls.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+lora_status lora_apply_linear_noalloc(int dtype, const void* x, void* y, int64_t T,
+                                      int64_t in_features, const int64_t* out_slices,
+                                      int32_t num_slices, const void* a, const void* b,
+                                      int32_t slots, int32_t R, const int32_t* token_order,
+                                      const int32_t* slot_indptr, const int32_t* ranks,
+                                      const float* scalings, void* stream);
+
+/* Size in bytes of lora_apply_linear_noalloc's static scratch array. */
+size_t lora_noalloc_scratch_bytes(void);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.lora_status_string(code)
     assert lib.lora_status_string(99) == b"unknown status"
     assert b"gfx950" in lib.lora_version()
@@ -183,3 +183,21 @@ def test_apply_linear_path_predicate(lib):
     assert f(1, -1, 4096, qkv, 3, 16) == -INVALID
     assert f(1, 256, 4096, qkv, 9, 16) == -UNSUPPORTED
     assert f(1, 256, 4096, _slices(12), 1, 16) == -ALIGN
+
+
+def test_noalloc_limits_checked_on_host(lib):
+    """lora_apply_linear_noalloc refuses sizes beyond its static scratch array
+    (LORA_ERR_SCRATCH_LIMIT) and bad scalars (as lora_apply_linear does)
+    before any HIP call, so these run without a GPU."""
+    SCRATCH_LIMIT = 6
+    assert lib.lora_noalloc_scratch_bytes() == 128 << 20
+    f = lib.lora_apply_linear_noalloc
+    qkv = _slices(4096, 1024, 1024)
+    # h alone of 2^20 tokens x 48 columns x 4 bytes = 192 MiB
+    assert lib.lora_apply_linear_workspace_bytes(1 << 20, 4096, 32, 3, 16) > 128 << 20
+    assert f(1, A16, A16, 1 << 20, 4096, qkv, 3, A16, A16, 32, 16, A16, A16, A16, A16,
+             None) == SCRATCH_LIMIT
+    assert f(1, A16, A16, 256, 4096, qkv, 3, A16, A16, 32, 0, A16, A16, A16, A16,
+             None) == UNSUPPORTED                                  # R = 0
+    assert f(1, A16, A16, -5, 4096, qkv, 3, A16, A16, 32, 16, A16, A16, A16, A16,
+             None) == INVALID                                      # T < 0
