@@ -27,7 +27,12 @@ SOURCES = ["addressing.hip", "gather_shrink.hip", "shrink.hip", "expand.hip", "f
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept off: the compiler must not form v_pk_* fp32
 # instructions from ordinary float code on this part.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The atomic optimizer is off: it rewrites a single lane's fetch_add into a
+# wave-wide one whose per-lane result it computes right after the atomic,
+# which puts a wait for the atomic's round trip in front of the loads that
+# follow it (the decode pieces take their tickets first and use them last).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wno-unused-command-line-argument"]
 

@@ -167,24 +167,40 @@ __device__ __forceinline__ void expand_range(char* __restrict__ y, int out, cons
 //    tiles and y rows, wait until the KP partial tiles of (s, i) are there,
 //    add them in kp order (deterministic), scale, split into bf16 hi + lo and
 //    expand.
-// Handoff: every expand piece (s, c) owns a counter pair {count, base}. Each
-// shrink piece of (s, i), once its partial tile is stored, adds 1 to the
-// count of every chunk of slice i; the expand piece waits until
-// count - base >= KP and then advances base by KP, so nothing is ever reset
-// and the pairs stay consistent across calls of any shape (count and base of
-// a chunk advance by the same KP in every call that uses it).
-// Memory ordering: the partial tiles are written and read only with
-// agent-scope atomic stores and loads, which are coherent across the XCDs
-// (they are performed at the device coherence point, not in an XCD's L2);
-// each producer waits for its stores to complete (s_waitcnt vmcnt(0)) before
-// the workgroup barrier that precedes the count update, and consumers issue
-// the tile loads only after observing the count. No L2 writeback is needed
-// because no plain (non-atomic) store is read across workgroups.
+// Handoff: every partial tile (s, i, kp) has a ticket counter in the
+// workspace, and every entry of the tile is one 64-bit word holding the fp32
+// value and a 32-bit tag. Each call touching tile j adds exactly kTicket to
+// its counter: the producer adds kTicket - nc and each of the nc expand pieces
+// of slice i adds 1, all at their start, off the critical path. Every
+// participant's fetch_add returns a value in [C, C + kTicket) where C, the
+// counter at the call's start, is a multiple of kTicket, so all of them
+// derive the same epoch E = C / kTicket + 1 without talking to each other.
+// The producer stores each entry as {value, tag(E)} in one agent-scope
+// atomic 64-bit store; an expand piece polls one entry per tile until it
+// carries tag(E), then loads the whole tile and takes each entry whose tag
+// matches (re-polling any that has not landed yet). Data and flag travel in
+// the same word, so the chain from the producer's last product to the
+// consumer's use is one store and one load (the earlier design stored the
+// tile, waited for the stores to complete, bumped a count, polled the count
+// and only then loaded the tile).
+// Why a stale entry is never taken for a new one: the tile's address and
+// size depend only on its index j and the rank bucket RT (16 x 16*RT
+// entries), the tag holds log2(RT) in its low 3 bits, and the counter of j
+// only grows, so an entry left at the same address by an earlier call either
+// has another rank bucket or an older epoch. (The epoch field holds 29 bits
+// and the counter 32: a stale entry could match again only after 2^25 calls
+// touching tile j, none of them in its rank bucket.)
+// Memory ordering: entries are written and read only with agent-scope
+// atomic 64-bit accesses, coherent across the XCDs; no other memory carries
+// the handoff, so no fence is needed. The counters need a zero-filled
+// workspace before its first use (any multiple of kTicket works).
 // The wait is bounded: a piece that times out (its producers not resident,
-// e.g. the GPU shared with other work) computes the slice's h itself and
-// still advances its base, so the kernel always finishes with the right
-// result and the counters stay consistent.
+// e.g. the GPU shared with other work) computes the slice's h itself, so the
+// kernel always finishes with the right result; its ticket was taken at the
+// start, so the counters stay multiples of kTicket.
 // ---------------------------------------------------------------------------
+
+constexpr uint32_t kTicket = 128;   // > 1 producer + the most expand pieces of a slice
 
 struct DecodeArgs {
   rsrc_t x_r, y_r;
@@ -192,7 +208,12 @@ struct DecodeArgs {
   int T, in, out, R;
   int KP;
   int spin_limit;
+  uint32_t lg;   // log2 of the rank bucket RT: the low 3 bits of every tag
 };
+
+__device__ __forceinline__ uint32_t epoch_tag(uint32_t ticket, uint32_t lg) {
+  return ((ticket / kTicket + 1u) << 3) | lg;
+}
 
 // Token id of lane row m: one vector load per lane (index clamped into the
 // array). Issued before the bulk A / B loads, it is the oldest load in
@@ -201,6 +222,30 @@ struct DecodeArgs {
 __device__ __forceinline__ int lane_token(const int32_t* __restrict__ tokp, int T, int seg0,
                                           int m) {
   return tokp[min(seg0 + m, T - 1)];
+}
+
+// The same token id read through the scalar path: the slot's (at most 16)
+// ids are 16 consecutive entries of token_order from a uniform base, loaded
+// into scalar registers (s_load), and lane row m picks entry seg0 - base + m.
+// Scalar loads are counted apart from vector memory (lgkmcnt, not vmcnt), so
+// the x and y row addresses do not wait behind the vector loads and the
+// ticket atomic a piece issues first.
+__device__ __forceinline__ int lane_token_s(const int32_t* __restrict__ tokp, int T, int seg0,
+                                            int m) {
+  const int base = __builtin_amdgcn_readfirstlane(T >= kMT ? min(seg0, T - kMT) : 0);
+  int ids[kMT];
+  if (T >= kMT) {
+#pragma unroll
+    for (int k = 0; k < kMT; ++k) ids[k] = tokp[base + k];
+  } else {   // a batch of fewer than 16 tokens: T >= 1 whenever a piece runs
+#pragma unroll
+    for (int k = 0; k < kMT; ++k) ids[k] = tokp[min(k, T - 1)];
+  }
+  const int j = min(seg0 - base + m, kMT - 1);
+  int t = ids[0];
+#pragma unroll
+  for (int k = 1; k < kMT; ++k) t = j == k ? ids[k] : t;
+  return t;
 }
 
 // acc[nt] += x_block . A_rows(nt)^T for the first NT rank tiles, over K
@@ -394,15 +439,22 @@ __device__ __forceinline__ void expand_chunk(rsrc_t b_r, rsrc_t y_r, int R, int 
   }
 }
 
-// Shrink piece (s, i, kp).
+// Shrink piece (s, i, kp): its partial tile goes to `tile` (16 x RP tagged
+// entries); `cnt` is the tile's ticket counter, nc the expand pieces of
+// slice i.
 template <int RT, int NW>
 __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, int r, int seg0,
-                                             int n, float* part_out, int2* pairs, int nchunks,
-                                             int kp, float* red, int lane, int w, int tid) {
+                                             int n, uint64_t* tile, uint32_t* cnt, int nc,
+                                             int kp, float* red, int* lds_tag, int lane, int w,
+                                             int tid) {
   constexpr int RP = RT * 16;
+  uint32_t ticket = 0;
+  if (tid == 0)   // the oldest load in flight: its return is not waited for until the store
+    ticket = __hip_atomic_fetch_add(cnt, kTicket - (uint32_t)nc, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = lane_token(d.tokp, d.T, seg0, m);
+  const int t = lane_token_s(d.tokp, d.T, seg0, m);
   const bool live = m < n;
   const uint32_t rowA = (uint32_t)d.in * 2u;
   const int steps = (d.in + 31) / 32;
@@ -414,33 +466,40 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
   shrink_steps<RT, NW>(
       d.x_r, a_r, rowA, d.in, r, [&] { return live ? (uint32_t)t * rowA : kOOB; }, s0, s1, acc,
       m, kg, w);
+  // the ticket is first used here: the empty statement keeps the compiler
+  // from consuming it (and so waiting for the atomic's return) before the
+  // bulk loads above are issued
+  asm volatile("" : "+v"(ticket));
   store_partial<RT>(red + w * kMT * RP, acc, m, kg);
+  if (tid == 0) *lds_tag = (int)epoch_tag(ticket, d.lg);
   __syncthreads();
+  const uint64_t tag = (uint64_t)(uint32_t)*lds_tag << 32;
   for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
     float v = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) v += red[ww * kMT * RP + idx];
-    __hip_atomic_store(part_out + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(tile + idx, tag | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's tile stores have completed
-  __syncthreads();
-  if (tid < nchunks)
-    __hip_atomic_fetch_add(&pairs[tid].x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Expand piece (s, chunk [lo, hi) of slice i).
+// Expand piece (s, chunk [lo, hi) of slice i): `tiles` are the KP partial
+// tiles of (s, i), `cnts` their ticket counters.
 template <int RT, int NW>
 __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rsrc_t b_r, int r,
                                              float scale, int seg0, int n, int lo, int hi,
-                                             const float* part_in, int2* pair, float* red,
-                                             uint16_t* hhi, uint16_t* hlo, int* flag, int lane,
+                                             const uint64_t* tiles, uint32_t* cnts, float* red,
+                                             uint16_t* hhi, uint16_t* hlo, int* lds_tag, int lane,
                                              int w, int tid) {
   constexpr int RP = RT * 16;
   constexpr int RPS = RP + 4;
   constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;   // tiles per wave in flight
+  uint32_t ticket = 0;
+  if (tid < d.KP)   // one ticket per partial tile, taken first
+    ticket = __hip_atomic_fetch_add(cnts + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = lane_token(d.tokp, d.T, seg0, m);   // oldest load in flight
+  const int t = lane_token_s(d.tokp, d.T, seg0, m);
   const bool live = m < n;
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
@@ -450,37 +509,44 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   u32x2 yv[PT];
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
   load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, 0, bv, yv, m, kg, w);
+  // first use of the ticket: not before the prefetch above is issued
+  asm volatile("" : "+v"(ticket));
 
-  if (tid == 0) {
-    const int base = __hip_atomic_load(&pair->y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int it = 0;
-    while ((int)((uint32_t)__hip_atomic_load(&pair->x, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) -
-                 (uint32_t)base) < d.KP &&
-           it < d.spin_limit) {
-      __builtin_amdgcn_s_sleep(1);
-      ++it;
-    }
-    *flag = (it < d.spin_limit) ? 1 : 0;
-    __hip_atomic_store(&pair->y, (int)((uint32_t)base + (uint32_t)d.KP), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // Every thread polls its own entries of the KP tiles (bounded) and takes
+  // each one once it carries this call's tag. Polling starts once this
+  // piece's own prefetch has returned: by then the producers, whose loads
+  // were issued at the same time, are close to done, and fewer polls load
+  // the memory system while it still streams A and x. (A first stage in
+  // which one lane per tile polled a single entry cost a further load
+  // round trip, ~0.5 us of the kernel's span.)
+  if (tid < d.KP) lds_tag[tid] = (int)epoch_tag(ticket, d.lg);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (*flag) {
-    for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
-      float v = 0.0f;
-      for (int kp = 0; kp < d.KP; ++kp)
-        v += __hip_atomic_load(part_in + kp * kMT * RP + idx, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      v *= scale;
-      const uint32_t hb = to_bf16_bits(v);
-      const uint32_t lb = to_bf16_bits(v - __uint_as_float(hb << 16));
-      const int q = idx / RP;
-      const int j = idx - q * RP;
-      hhi[q * RPS + j] = (uint16_t)hb;
-      hlo[q * RPS + j] = (uint16_t)lb;
+  bool ok = true;
+  for (int idx = tid; idx < kMT * RP; idx += NW * kWave) {
+    float v = 0.0f;
+    for (int kp = 0; kp < d.KP; ++kp) {
+      const uint64_t* e = tiles + (size_t)kp * kMT * RP + idx;
+      const uint32_t tag = (uint32_t)lds_tag[kp];
+      uint64_t word = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int it = 0;
+      while ((uint32_t)(word >> 32) != tag && it < d.spin_limit) {
+        __builtin_amdgcn_s_sleep(2);
+        word = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++it;
+      }
+      ok = ok && (uint32_t)(word >> 32) == tag;
+      v += __uint_as_float((uint32_t)word);
     }
-  } else {
+    v *= scale;
+    const uint32_t hb = to_bf16_bits(v);
+    const uint32_t lb = to_bf16_bits(v - __uint_as_float(hb << 16));
+    const int q = idx / RP;
+    const int j = idx - q * RP;
+    hhi[q * RPS + j] = (uint16_t)hb;
+    hlo[q * RPS + j] = (uint16_t)lb;
+  }
+  if (!__syncthreads_and(ok)) {
     // producers not seen in time: compute this slice's h here
     const uint32_t rowA = (uint32_t)d.in * 2u;
     f32x4 acc[RT];
@@ -592,8 +658,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     const void* __restrict__ a_, const void* __restrict__ b_, int slots, int R,
     const int32_t* __restrict__ token_order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, const float* __restrict__ scalings, ChunkTable ct,
-    int n_shrink, int n_expand, int nclass, int KP, float* __restrict__ part,
-    int2* __restrict__ pairs, int spin_limit) {
+    int n_shrink, int n_expand, int nclass, int KP, uint64_t* __restrict__ part,
+    uint32_t* __restrict__ tickets, int spin_limit) {
   using L = Lds<RT, NW>;
   constexpr int RP = RT * 16;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -652,19 +718,23 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     d.R = R;
     d.KP = KP;
     d.spin_limit = spin_limit;
+    d.lg = RT == 1 ? 0u : RT == 2 ? 1u : RT == 4 ? 2u : RT == 8 ? 3u : 4u;
     const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * SR + (int64_t)i * R) * in * 2,
                                  (uint32_t)r * (uint32_t)in * 2u);
-    float* pbase = part + ((int64_t)s * S + i) * KP * kMT * RP;
-    int2* slot_pairs = pairs + (int64_t)s * kMaxChunks;
+    // the KP partial tiles of (s, i) and their ticket counters: tile index
+    // j = (s * S + i) * KP + kp
+    const int64_t j0 = ((int64_t)s * S + i) * KP;
+    uint64_t* tiles = part + j0 * kMT * RP;
+    uint32_t* cnts = tickets + j0;
     if (is_shrink) {
       const int kp = rem - i * KP;
-      shrink_piece<RT, NW>(d, a_r, r, seg0, n, pbase + kp * kMT * RP,
-                           slot_pairs + ct.first[i], ct.per_slice[i], kp, red, lane, w, tid);
+      shrink_piece<RT, NW>(d, a_r, r, seg0, n, tiles + kp * kMT * RP, cnts + kp,
+                           ct.per_slice[i], kp, red, scratch, lane, w, tid);
     } else {
       const rsrc_t b_r =
           make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
-      expand_piece<RT, NW>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem], pbase,
-                           slot_pairs + rem, red, hhi, hlo, scratch + 20, lane, w, tid);
+      expand_piece<RT, NW>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem], tiles,
+                           cnts, red, hhi, hlo, scratch, lane, w, tid);
     }
     return;
   }
@@ -854,18 +924,20 @@ ChunkTable make_chunks(const SliceTable& st, int R) {
 }  // namespace
 
 size_t counter_bytes(int slots, int S) {
-  // fixed size (a {count, base} pair for every slot and chunk index), so
-  // calls of different shapes share one workspace without their regions
+  // fixed size: a ticket counter for every partial tile index any call can
+  // use (8192 slots x 8 slices x 8 K parts = 2^19; 2^20 reserved), so calls
+  // of different shapes share one workspace without their regions
   // overlapping
   (void)slots;
   (void)S;
-  return (size_t)8192 * kMaxChunks * 2 * sizeof(int);
+  return (size_t)1 << 22;
 }
 
 size_t fused_partial_bytes(int slots, int S, int R, int in) {
   const int RP = rt_bucket(R) * 16;
-  // room for the most parts any output width takes
-  return (size_t)slots * S * k_parts(in, 0) * kMT * RP * 4;
+  // room for the most parts any output width takes; 8 bytes per entry
+  // (value and tag)
+  return (size_t)slots * S * k_parts(in, 0) * kMT * RP * sizeof(uint64_t);
 }
 
 bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in) {
@@ -898,8 +970,8 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int64_t n_prefill = (T + kMT - 1) / kMT + slots;
   const int64_t grid = n_shrink + n_expand + n_prefill;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  int2* pairs = (int2*)workspace;
-  float* part = (float*)((char*)workspace + counter_bytes(slots, st.n));
+  uint32_t* tickets = (uint32_t*)workspace;
+  uint64_t* part = (uint64_t*)((char*)workspace + counter_bytes(slots, st.n));
   // bound of the wait of an expand piece (iterations of ~0.1-1 us); 0 makes
   // every expand piece compute h itself (used by the tests of that path)
   const int spin_limit = env_int("LORA_SPIN_LIMIT", 1 << 13);
@@ -914,7 +986,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
     }                                                                                           \
     hipLaunchKernelGGL((k_apply_fused<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,    \
                        stream, x, y, T, in, st, a, b, slots, R, token_order, indptr, ranks,     \
-                       scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part, pairs,      \
+                       scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part, tickets,    \
                        spin_limit);                                                             \
   } while (0)
   switch (rt) {
