@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 __all__ = [
     "Addressing", "LoraError", "lib", "lib_path", "build_addressing", "shrink",
     "gather_shrink", "expand_", "expand_fused", "apply_linear_", "apply_", "Backend",
-    "workspace_bytes", "STATUS",
+    "workspace_bytes", "STATUS", "column_linear", "fused_column_linear",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,10 @@ SIGNATURES = {
     "lora_apply_linear_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P,
                                                  _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "lora_noalloc_scratch_bytes": (_SZ, []),
+    "lora_column_linear": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _I64, _I64, _P, _I32, _P]),
+    "lora_fused_column_linear": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _I64, _I64, _P, _I32,
+                                                _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lora_fused_column_linear_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32]),
 }
 
 
@@ -312,6 +316,51 @@ def apply_(x, y, a, b, addressing, ranks, scalings, out_slices: Sequence[int],
         expand_(h, b, addressing, ranks, scalings, y, out_slices)
     else:
         apply_linear_(x, y, a, b, addressing, ranks, scalings, out_slices)
+    return y
+
+
+def column_linear(x, w, out_slices: Sequence[int], y=None):
+    """The base projection of a fused column linear layer, y = x @ W^T
+    (W [out, in]: the shards stacked along the output dimension)."""
+    import torch
+    dev = _dev(x, w, y)
+    T, in_f = x.shape
+    out = int(sum(out_slices))
+    if w.shape != (out, in_f) or x.dtype != w.dtype:
+        raise LoraError("shape/dtype mismatch between x, w and out_slices")
+    if y is None:
+        y = torch.empty(T, out, dtype=x.dtype, device=dev)
+    arr, S = _slices(out_slices)
+    st = lib().lora_column_linear(_dtype_code(x), _ptr(x), _ptr(w), _ptr(y), T, in_f,
+                                  ctypes.cast(arr, _P), S, _stream(dev))
+    _check(st, "lora_column_linear")
+    return y
+
+
+def fused_column_linear(x, w, a, b, addressing, ranks, scalings, out_slices: Sequence[int],
+                        y=None, workspace=None):
+    """The base projection x @ W^T with each token's LoRA delta added in the
+    product's epilogue (y written once); returns y."""
+    import torch
+    order, indptr = _addr(addressing)
+    ranks = _i32(ranks)
+    dev = _dev(x, w, a, b, order, indptr, ranks, scalings, y)
+    T, in_f = x.shape
+    slots, out, R = b.shape
+    S = len(out_slices)
+    if w.shape != (out, in_f) or a.shape != (slots, S * R, in_f) or sum(out_slices) != out:
+        raise LoraError("shape mismatch in fused_column_linear")
+    if y is None:
+        y = torch.empty(T, out, dtype=x.dtype, device=dev)
+    need = int(lib().lora_fused_column_linear_workspace_bytes(T, in_f, S, R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    arr, S = _slices(out_slices)
+    st = lib().lora_fused_column_linear(
+        _dtype_code(x), _ptr(x), _ptr(w), _ptr(y), T, in_f, ctypes.cast(arr, _P), S, _ptr(a),
+        _ptr(b), slots, R, _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(scalings),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "lora_fused_column_linear")
     return y
 
 

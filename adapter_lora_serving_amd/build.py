@@ -22,7 +22,7 @@ LIB_NAME = "liblora_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["addressing.hip", "gather_shrink.hip", "shrink.hip", "expand.hip", "fused.hip",
-           "sgmv.hip", "noalloc.hip", "lora_api.cpp"]
+           "sgmv.hip", "linear_lora.hip", "noalloc.hip", "lora_api.cpp"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept off: the compiler must not form v_pk_* fp32

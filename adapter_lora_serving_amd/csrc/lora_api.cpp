@@ -259,6 +259,73 @@ lora_status lora_expand(int dtype, void* y, int64_t T, const int64_t* out_slices
   return hip_status(e);
 }
 
+size_t lora_fused_column_linear_workspace_bytes(int64_t T, int64_t in_features,
+                                                int32_t num_slices, int32_t R) {
+  if (T < 0 || T > kMaxI32 || num_slices < 1 || num_slices > lora::kMaxSlices || R < 1 ||
+      R > 256 || in_features < 1 || in_features > kMaxI32)
+    return 0;
+  // h, then the shrink's K parts
+  return ws_h_bytes(T, num_slices, R) +
+         lora_shrink_workspace_bytes(T, in_features, num_slices, R);
+}
+
+lora_status lora_column_linear(int dtype, const void* x, const void* w, void* y, int64_t T,
+                               int64_t in_features, const int64_t* out_slices,
+                               int32_t num_slices, void* stream) {
+  if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || T > kMaxI32 || in_features < 1 || in_features > kMaxI32)
+    return LORA_ERR_INVALID_ARG;
+  SliceTable tab;
+  lora_status st = make_slices(dtype, out_slices, num_slices, 8, &tab);
+  if (st != LORA_OK) return st;
+  if (!lora::linear_lora_supported(dtype, tab, 8, (int)T, (int)in_features))
+    return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  if (!x || !w || !y) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return LORA_ERR_ALIGNMENT;
+  // no delta: the token order is the identity, so no addressing is needed
+  return hip_status(lora::launch_linear_lora(x, w, y, (int)T, (int)in_features, tab, nullptr,
+                                             nullptr, 1, 8, nullptr, nullptr, nullptr, nullptr,
+                                             (hipStream_t)stream));
+}
+
+lora_status lora_fused_column_linear(int dtype, const void* x, const void* w, void* y, int64_t T,
+                                     int64_t in_features, const int64_t* out_slices,
+                                     int32_t num_slices, const void* a, const void* b,
+                                     int32_t slots, int32_t R, const int32_t* token_order,
+                                     const int32_t* slot_indptr, const int32_t* ranks,
+                                     const float* scalings, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (dtype != LORA_BF16) return LORA_ERR_UNSUPPORTED;
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  SliceTable tab;
+  if ((st = make_slices(dtype, out_slices, num_slices, R, &tab)) != LORA_OK) return st;
+  if (in_features < 1 || in_features > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (!lora::linear_lora_supported(dtype, tab, R, (int)T, (int)in_features))
+    return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  if (!x || !w || !y || !a || !b || !scalings) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(a) || !aligned16(b))
+    return LORA_ERR_ALIGNMENT;
+  if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  const size_t need = lora_fused_column_linear_workspace_bytes(T, in_features, num_slices, R);
+  if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  // h of every token (zeros where the expand does not read), then the base
+  // projection with the delta of h in its epilogue
+  float* h = static_cast<float*>(workspace);
+  const size_t hb = ws_h_bytes(T, num_slices, R);
+  const size_t pb = workspace_bytes - hb;
+  st = lora_shrink(dtype, x, T, in_features, a, slots, num_slices, R, token_order, slot_indptr,
+                   ranks, h, pb > 0 ? static_cast<char*>(workspace) + hb : nullptr, pb, stream);
+  if (st != LORA_OK) return st;
+  return hip_status(lora::launch_linear_lora(x, w, y, (int)T, (int)in_features, tab, h, b, slots,
+                                             R, token_order, slot_indptr, ranks, scalings,
+                                             (hipStream_t)stream));
+}
+
 int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int64_t* out_slices,
                            int32_t num_slices, int32_t R) {
   if (dtype != LORA_F32 && dtype != LORA_BF16) return -LORA_ERR_UNSUPPORTED;

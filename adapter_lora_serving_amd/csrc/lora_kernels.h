@@ -109,4 +109,15 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const int32_t* ranks, const float* scalings, void* workspace,
                               hipStream_t stream);
 
+// The base projection y = x @ W^T of a fused linear layer (W [out, in], the
+// shards stacked along out) with the LoRA delta of h (fp32 [T, S*R], from
+// the shrink; nullptr: no delta) added before y is stored. Supported: bf16,
+// every slice width a multiple of 256, `in` a multiple of 8, every buffer
+// below 2 GiB.
+bool linear_lora_supported(int dtype, const SliceTable& st, int R, int T, int in);
+hipError_t launch_linear_lora(const void* x, const void* w, void* y, int T, int in,
+                              const SliceTable& st, const float* h, const void* b, int slots,
+                              int R, const int32_t* token_order, const int32_t* indptr,
+                              const int32_t* ranks, const float* scalings, hipStream_t stream);
+
 }  // namespace lora

@@ -140,6 +140,160 @@ def cpu_baseline(wl, tg, budget_s: float):
             "cpu_model": model, "affinity_cpus": int(affinity), "blas": blas}
 
 
+def _graph_timer(torch, stream):
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        g.replay()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            st.record(stream)
+            g.replay()
+            en.record(stream)
+        torch.cuda.synchronize()
+        return st.elapsed_time(en)
+
+    return capture, timed
+
+
+def run_fused_linear(args, torch, L, dev):
+    """The base projection of a linear target with the LoRA delta fused into
+    its epilogue (lora_fused_column_linear: the shrink into the workspace,
+    then the MFMA GEMM whose epilogue adds the delta), against the same GEMM
+    followed by lora_apply_linear, and against the library GEMM (torch.matmul,
+    hipBLASLt) followed by lora_apply_linear. A step is one addressing build
+    plus one fused call."""
+    config = args.config if args.config != 2 or args.target else 3
+    wl = W.make_config(config, seed=0)
+    tg = wl.target(args.target or ("gate_up" if config == 3 else None))
+    w_host = W.base_weight(wl, tg)
+    alg_bytes_lora, lora_flops, _ = workload_cost(wl, tg)
+    T, in_f, out = wl.T, tg.in_features, tg.out_features
+    base_flops = 2 * T * in_f * out
+    flops = base_flops + lora_flops
+    # minimum HBM bytes of the fused call: x, W, A and B of the used slots,
+    # y written once, metadata
+    e = 2
+    min_bytes = e * (T * in_f + out * in_f + T * out) + alg_bytes_lora - 2 * e * T * out - e * T * in_f
+
+    def d(arr):
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ranks = torch.from_numpy(wl.ranks).to(dev)
+    scal = torch.from_numpy(wl.scalings).to(dev)
+    ts = torch.from_numpy(wl.token_slot.astype(np.int32)).to(dev)
+    set_bytes = e * (T * in_f + out * in_f + T * out) + (tg.a.size + tg.b.size) * e
+    n_sets = args.sets or int(min(16, max(2, math.ceil(1.1 * 2 ** 30 / set_bytes))))
+    eprint(f"fused_linear {wl.name}/{tg.name}: T={T} in={in_f} out={tg.out_slices} R={wl.R} "
+           f"slots={wl.slots}; {base_flops / 1e9:.1f} GFLOP base + {lora_flops / 1e9:.2f} GFLOP "
+           f"delta; {n_sets} buffer sets x {set_bytes / 1e6:.0f} MB")
+    x0, w0, a0, b0 = d(tg.x), d(w_host), d(tg.a), d(tg.b)
+    sets = []
+    for i in range(n_sets):
+        s = dict(x=x0.clone(), w=w0.clone(), a=a0.clone(), b=b0.clone(),
+                 y=torch.empty(T, out, dtype=torch.bfloat16, device=dev), ts=ts.clone())
+        s["addr"] = L.build_addressing(s["ts"], wl.slots)
+        sets.append(s)
+    del x0, w0, a0, b0
+    need = int(L.lib().lora_fused_column_linear_workspace_bytes(T, in_f, tg.num_slices, wl.R))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    wsa = torch.zeros(L.workspace_bytes(T, in_f, wl.slots, tg.num_slices, wl.R),
+                      dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        s = sets[i % n_sets]
+        L.fused_column_linear(s["x"], s["w"], s["a"], s["b"], s["addr"], ranks, scal,
+                              tg.out_slices, y=s["y"], workspace=ws)
+
+    def step(i):
+        s = sets[i % n_sets]
+        L.build_addressing(s["ts"], wl.slots, out=s["addr"])
+        fused(i)
+
+    def base_only(i):
+        s = sets[i % n_sets]
+        L.column_linear(s["x"], s["w"], tg.out_slices, y=s["y"])
+
+    def unfused(i):
+        s = sets[i % n_sets]
+        L.column_linear(s["x"], s["w"], tg.out_slices, y=s["y"])
+        L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal, tg.out_slices,
+                        workspace=wsa)
+
+    def lib_base(i):
+        s = sets[i % n_sets]
+        torch.matmul(s["x"], s["w"].t(), out=s["y"])
+
+    def lib_unfused(i):
+        lib_base(i)
+        s = sets[i % n_sets]
+        L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal, tg.out_slices,
+                        workspace=wsa)
+
+    for i in range(args.warmup):
+        step(i)
+        unfused(i)
+        lib_unfused(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    capture, timed = _graph_timer(torch, stream)
+    K = args.steps
+    ms = {}
+    for name, fn in (("step", step), ("fused", fused), ("base", base_only), ("unfused", unfused),
+                     ("lib_base", lib_base), ("lib_unfused", lib_unfused)):
+        g = capture(fn, K)
+        ms[name] = timed(g) / K
+        del g
+    us = {k: round(v * 1e3, 2) for k, v in ms.items()}
+    tf = flops / (ms["fused"] * 1e-3) / 1e12
+    tf_base = base_flops / (ms["base"] * 1e-3) / 1e12
+    eprint(f"per call (us): {us}; fused {tf:.0f} TFLOP/s, base GEMM alone {tf_base:.0f} TFLOP/s")
+    result = {
+        "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill)",
+        "value": round(T / (ms["step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms["step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs and base weights, no trained adapters)",
+        "config": {"workload": "fused_linear_" + wl.name, "target": tg.name, "T": T,
+                   "in": in_f, "out_slices": list(tg.out_slices), "R": wl.R,
+                   "slots": wl.slots, "buffer_sets": n_sets},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "lora_fused_column_linear",
+            "achieved": round(tf, 1),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(f"fused_linear_{wl.name}_{tg.name}"),
+            "algorithmic_flops_per_launch": int(flops),
+            "min_hbm_bytes_per_launch": int(min_bytes),
+            "avg_launch_us": us["fused"],
+        },
+        "per_call_us": {"fused (shrink + GEMM with the delta in its epilogue)": us["fused"],
+                        "GEMM alone (lora_column_linear)": us["base"],
+                        "GEMM then lora_apply_linear": us["unfused"],
+                        "torch.matmul alone": us["lib_base"],
+                        "torch.matmul then lora_apply_linear": us["lib_unfused"]},
+        "gemm_tflops": round(tf_base, 1),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,14 +302,16 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="synthetic workload 1-5 (default 2)")
     ap.add_argument("--target", default=None, help="target name for multi-target workloads")
     ap.add_argument("--workload", choices=["router_fold", "tp8_qkv_decode", "tp8_prefill",
-                                           "moe_experts"],
+                                           "moe_experts", "fused_linear"],
                     default=None,
                     help="a workload beyond the five configs: router_fold (a router LoRA "
                          "folded onto 64 routing logits, decode batch); tp8_qkv_decode, "
                          "tp8_prefill (one GPU's share of a TP=8 projection; --target "
                          "gate_up or down for the latter); moe_experts (the routed-expert "
                          "LoRA on 512 expert-sorted rows, its addressing by (expert, slot); "
-                         "--target expert_gate_up or expert_down)")
+                         "--target expert_gate_up or expert_down); fused_linear (the base "
+                         "projection x @ W^T of --config/--target with the LoRA delta in its "
+                         "epilogue, lora_fused_column_linear; default config 3 gate_up)")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -175,6 +331,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.workload == "fused_linear":
+        return run_fused_linear(args, torch, L, dev)
     if args.workload == "router_fold":
         wl = W.make_router_fold(0)
     elif args.workload == "moe_experts":

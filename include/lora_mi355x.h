@@ -260,6 +260,59 @@ int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int6
                            int32_t num_slices, int32_t R);
 
 /*
+ * lora_column_linear: the base projection of a fused column-parallel linear
+ * layer, y = x @ W^T, on the library's bf16 MFMA GEMM.
+ *
+ * Source: page "mstar.model.components.linear", FusedColumnLinear (the
+ * shards of the fused projection, e.g. q, k, v or gate, up, are stacked
+ * along the output dimension in order and computed as one product).
+ * x [T, in], W [out, in], y [T, out] (written, not accumulated), all bf16,
+ * out = sum(out_slices) (host array, num_slices widths, each a multiple of
+ * 256); fp32 accumulation, one round-to-nearest-even per output. This is the
+ * same kernel lora_fused_column_linear runs, without a delta; it is the base
+ * half of "base projection, then lora_apply_linear".
+ * Errors: LORA_ERR_UNSUPPORTED for fp32, a width not a multiple of 256, `in`
+ * not a multiple of 8 or a buffer of 2 GiB or more.
+ */
+lora_status lora_column_linear(int dtype, const void* x, const void* w, void* y, int64_t T,
+                               int64_t in_features, const int64_t* out_slices,
+                               int32_t num_slices, void* stream);
+
+/*
+ * lora_fused_column_linear: the base projection with the LoRA delta fused
+ * into its epilogue:
+ *   y[t, :] = x[t] @ W^T  +  (for each slice i) scalings[s] * h[t, slice i]
+ *             @ B[s, slice i]^T,  h = shrink(x) as lora_shrink, s = slot(t).
+ *
+ * Source: page "mstar.model.components.linear", FusedColumnLinear (the base
+ * product over the stacked shards), page "mstar.engine.resources.lora.
+ * backend", LoraBackend.apply_linear_ (the delta), and page
+ * "spark_model/lora/target.rs", module overview (kernels that fuse the delta
+ * into the base projection's epilogue). The delta is added to the product's
+ * fp32 accumulators before the single rounding of y, so y is written once
+ * and never read: the same result as lora_column_linear followed by
+ * lora_apply_linear up to that one rounding, without the delta's
+ * read-modify-write of y.
+ * Arguments as lora_column_linear plus those of lora_apply_linear (a, b,
+ * slots, R, the addressing, ranks, scalings); dead tokens and rank-0 slots
+ * get the base projection only. workspace (device, required, 256-byte
+ * aligned, no initialisation needed): at least
+ * lora_fused_column_linear_workspace_bytes(T, in, num_slices, R) bytes
+ * (h and the shrink's K parts). Calls sharing a workspace must not overlap.
+ */
+lora_status lora_fused_column_linear(int dtype, const void* x, const void* w, void* y, int64_t T,
+                                     int64_t in_features, const int64_t* out_slices,
+                                     int32_t num_slices, const void* a, const void* b,
+                                     int32_t slots, int32_t R, const int32_t* token_order,
+                                     const int32_t* slot_indptr, const int32_t* ranks,
+                                     const float* scalings, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_fused_column_linear needs (0 on bad input). */
+size_t lora_fused_column_linear_workspace_bytes(int64_t T, int64_t in_features,
+                                                int32_t num_slices, int32_t R);
+
+/*
  * lora_apply_linear_noalloc: lora_apply_linear without a workspace argument,
  * for callers that cannot allocate device memory (code under graph capture,
  * tight serving loops, harnesses that forbid the allocator).

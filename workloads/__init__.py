@@ -27,7 +27,7 @@ BF16_NAN = np.uint16(0x7FC0)
 __all__ = [
     "Target", "Workload", "f32_to_bf16_bits", "make_workload", "make_config",
     "CONFIG_NAMES", "poison_unread", "zipf_request_lengths", "permute_tokens",
-    "take_tokens", "with_token_slot", "make_moe_experts", "make_router_fold", "make_tp_share",
+    "take_tokens", "with_token_slot", "base_weight", "make_moe_experts", "make_router_fold", "make_tp_share",
 ]
 
 
@@ -245,6 +245,18 @@ def make_moe_experts(seed: int = 0, *, T: int = 256, experts: int = 8, topk: int
     wl.experts = dict(experts=experts, slots=slots, row_slot=row_slot.astype(np.int32),
                       offsets=offsets.astype(np.int32))
     return wl
+
+
+def base_weight(wl: Workload, tg: Target) -> np.ndarray:
+    """The base projection's weight W [out, in] of a linear target (the
+    shards of its out slices stacked in order), N(0, 1/in) so that x @ W^T is
+    of unit scale like y0, in the workload's dtype. Drawn from a generator of
+    its own, seeded by the workload's seed and the target's position, so the
+    workload's other draws are the same with or without it."""
+    idx = next(k for k, t in enumerate(wl.targets) if t is tg)
+    rng = np.random.default_rng([int(wl.seed), 7919, idx])
+    return _gauss(rng, (tg.out_features, tg.in_features), 1.0 / np.sqrt(tg.in_features),
+                  wl.dtype)
 
 
 def with_token_slot(wl: Workload, token_slot: np.ndarray) -> Workload:
