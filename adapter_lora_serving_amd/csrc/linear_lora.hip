@@ -39,14 +39,19 @@ namespace lora {
 namespace {
 
 constexpr int kGT = 256;         // tile rows and columns
-constexpr int kGK = 64;          // K per stage
+constexpr int kGK = 32;          // K per stage
+constexpr int kStages = 4;       // LDS ring: the stage being read + 3 in flight
 constexpr int kGThreads = 256;
-constexpr int kStageBytes = kGT * kGK * 2;   // one operand tile, bf16
-// LDS: [x stage 0][x stage 1][W stage 0][W stage 1][token ids]
-constexpr int kLdsX = 0;
-constexpr int kLdsW = 2 * kStageBytes;
-constexpr int kLdsTok = 4 * kStageBytes;
+constexpr int kStageBytes = kGT * kGK * 2;   // one operand tile of one stage, bf16 (16 KB)
+// LDS: stage s holds [x tile][W tile] at s * 2 * kStageBytes; then token ids
+constexpr int kLdsTok = kStages * 2 * kStageBytes;
 constexpr int kGemmLds = kLdsTok + kGT * 4 + 64;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt operand that waits until at most n vector memory operations are
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for)
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // D[16x16] += A[16 x 32] . B[16 x 32]^T (v_mfma_f32_16x16x32_bf16): lane
 // (m, g) gives row m, k in [8g, 8g + 8) of both operands and receives
@@ -55,10 +60,12 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// byte offset of 16-byte chunk c of row `row` in a tile of 8 chunks per row
-__device__ __forceinline__ int swz8(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
-// the same for 4 chunks per row (a 32-rank epilogue tile)
-__device__ __forceinline__ int swz4(int row, int c) { return row * 64 + ((c ^ (row & 3)) << 4); }
+// byte offset of 16-byte chunk c of row `row` in a tile of 4 chunks (64 B)
+// per row: chunk c sits at c ^ ((row >> 1) & 3), so the 16-byte MFMA operand
+// reads of 8 consecutive rows (one chunk each) cover all 32 banks once
+__device__ __forceinline__ int swz4(int row, int c) {
+  return row * 64 + ((c ^ ((row >> 1) & 3)) << 4);
+}
 
 }  // namespace
 
@@ -79,16 +86,24 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   const int m = lane & 15;
   const int g = lane >> 4;
 
-  // tiles in XCD-contiguous ranges: block b runs on XCD b % 8 and takes
-  // tile (b % 8) * per + b / 8, so the tiles one XCD runs are consecutive
-  // (same W column block over neighbouring token blocks) and share its L2
+  // tile order: block b runs on XCD b % 8 and takes position
+  // (b % 8) * per + b / 8 of a grouped order (8 token blocks at a time, the
+  // token block varying fastest), so the ~32 tiles an XCD runs at once are
+  // 8 token blocks x 4 column blocks: each x block is read by 4 of them and
+  // each W block by 8 from the XCD's L2 (a single column block against 32
+  // token blocks would stream 33 operand blocks per window instead of 12)
   const int G = mtiles * ntiles;
   const int per = (G + 7) / 8;
   const int bid = blockIdx.x;
-  const int tile = (bid & 7) * per + (bid >> 3);
-  if (tile >= G) return;
-  const int tn = tile / mtiles;
-  const int tm = tile - tn * mtiles;
+  const int L = (bid & 7) * per + (bid >> 3);
+  if (L >= G) return;
+  constexpr int kGroupM = 8;
+  const int grp = L / (kGroupM * ntiles);
+  const int fm = grp * kGroupM;
+  const int gsz = min(kGroupM, mtiles - fm);
+  const int li = L - grp * kGroupM * ntiles;
+  const int tm = fm + li % gsz;
+  const int tn = li / gsz;
   const int m0 = tm * kGT;
   const int n0 = tn * kGT;
 
@@ -104,34 +119,34 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   const rsrc_t w_r = make_rsrc(w_, (uint32_t)out * (uint32_t)in * 2u);
   const uint32_t rowb = (uint32_t)in * 2u;
 
-  // global -> LDS: thread loads chunk (tid & 7) of rows (tid >> 3) + 32 j
-  const int lc = tid & 7;
-  const int lr = tid >> 3;
-  uint32_t xoff[8], woff[8];
+  // global -> LDS without registers (buffer_load ... lds): one instruction
+  // of a wave fills a contiguous 1 KB block of LDS, lane L at byte 16 L, i.e.
+  // rows 16 blk + L / 4, physical chunk L & 3 of a 64-byte row; the lane
+  // fetches the logical chunk stored there (the swizzle is undone on the
+  // global side). Wave w fills blocks w, w + 4, w + 8, w + 12 of both the x
+  // and the W tile of a stage: 8 instructions per wave per stage.
+  const int pr = lane >> 2;                          // row within the block
+  const int pc = (lane & 3) ^ ((pr >> 1) & 3);       // logical chunk of the lane
+  uint32_t xoff[4], woff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = lr + 32 * j;
+  for (int j = 0; j < 4; ++j) {
+    const int row = (w + 4 * j) * 16 + pr;
     const int t = tok[row];
-    xoff[j] = t >= 0 ? (uint32_t)t * rowb + (uint32_t)lc * 16u : kOOB;
-    woff[j] = n0 + row < out ? (uint32_t)(n0 + row) * rowb + (uint32_t)lc * 16u : kOOB;
+    xoff[j] = t >= 0 ? (uint32_t)t * rowb + (uint32_t)pc * 16u : kOOB;
+    woff[j] = n0 + row < out ? (uint32_t)(n0 + row) * rowb + (uint32_t)pc * 16u : kOOB;
   }
-  u32x4 xs[8], ws[8];
-  auto gload = [&](int k0) {
-    const bool kv = k0 + lc * 8 < in;
+  auto issue = [&](int stage, int k0) {
+    const bool kv = k0 + pc * 8 < in;
+    char* sb = lds + (stage % kStages) * 2 * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      xs[j] = bload16(x_r, kv && xoff[j] != kOOB ? xoff[j] + (uint32_t)k0 * 2u : kOOB);
-      ws[j] = bload16(w_r, kv && woff[j] != kOOB ? woff[j] + (uint32_t)k0 * 2u : kOOB);
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* xb = lds + kLdsX + buf * kStageBytes;
-    char* wb = lds + kLdsW + buf * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = lr + 32 * j;
-      *(u32x4*)(xb + swz8(row, lc)) = xs[j];
-      *(u32x4*)(wb + swz8(row, lc)) = ws[j];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = w + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_r, (lds_void*)(sb + blk * 1024), 16,
+          kv && xoff[j] != kOOB ? xoff[j] + (uint32_t)k0 * 2u : kOOB, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_r, (lds_void*)(sb + kStageBytes + blk * 1024), 16,
+          kv && woff[j] != kOOB ? woff[j] + (uint32_t)k0 * 2u : kOOB, 0, 0, 0);
     }
   };
 
@@ -141,35 +156,44 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // products of one 32-deep K step from LDS (x rows and W rows of 8 chunks)
-  auto kstep = [&](const char* xb, const char* wb, int c) {
+  const int kt = (in + kGK - 1) / kGK;
+  // three stages in flight before the loop
+  for (int st0 = 0; st0 < kStages - 1 && st0 < kt; ++st0) issue(st0, st0 * kGK);
+  for (int it = 0; it < kt; ++it) {
+    // this stage's loads are done once at most the later stages' (8 per
+    // stage per wave) are outstanding; then the barrier makes every wave's
+    // part visible, and frees the buffer read in the previous iteration
+    const int ahead = min(kt - 1 - it, kStages - 2);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_le(16));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(8));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+    // a plain s_barrier: __syncthreads()'s release fence would wait for every
+    // load in flight (LDS DMA counts as vector memory) and so empty the ring;
+    // the empty asm statements keep the compiler from moving LDS accesses
+    // across it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + kStages - 1 < kt) issue(it + kStages - 1, (it + kStages - 1) * kGK);
+    const char* xb = lds + (it % kStages) * 2 * kStageBytes;
+    const char* wb = xb + kStageBytes;
     bf16x8 wo[8], xo[8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-      wo[a] = *(const bf16x8*)(wb + swz8(wn * 128 + a * 16 + m, c + g));
+      wo[a] = *(const bf16x8*)(wb + swz4(wn * 128 + a * 16 + m, g));
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-      xo[a] = *(const bf16x8*)(xb + swz8(wm * 128 + a * 16 + m, c + g));
+      xo[a] = *(const bf16x8*)(xb + swz4(wm * 128 + a * 16 + m, g));
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int bq = 0; bq < 8; ++bq) acc[a][bq] = mfma32(wo[a], xo[bq], acc[a][bq]);
-  };
-
-  const int kt = (in + kGK - 1) / kGK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int it = 0; it < kt; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < kt) gload((it + 1) * kGK);
-    const char* xb = lds + kLdsX + buf * kStageBytes;
-    const char* wb = lds + kLdsW + buf * kStageBytes;
-    kstep(xb, wb, 0);
-    kstep(xb, wb, 4);
-    if (it + 1 < kt) lstore(buf ^ 1);
-    __syncthreads();
+    // all 16 operand reads first, then the 64 products (each waits only for
+    // its own operands), instead of a full LDS wait before every 8 products
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
   }
+  __syncthreads();   // the epilogue reuses the ring
 
   // ---- LoRA epilogue ----------------------------------------------------
   if (h != nullptr && m0 < T) {
