@@ -238,24 +238,26 @@ def run_fused_linear(args, torch, L, dev):
         L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal, tg.out_slices,
                         workspace=wsa)
 
+    legs = [("step", step), ("fused", fused)]
+    if not args.no_compare:
+        legs += [("base", base_only), ("unfused", unfused), ("lib_base", lib_base),
+                 ("lib_unfused", lib_unfused)]
     for i in range(args.warmup):
-        step(i)
-        unfused(i)
-        lib_unfused(i)
+        for _, fn in legs[1:] if len(legs) > 2 else legs:
+            fn(i)
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     capture, timed = _graph_timer(torch, stream)
     K = args.steps
     ms = {}
-    for name, fn in (("step", step), ("fused", fused), ("base", base_only), ("unfused", unfused),
-                     ("lib_base", lib_base), ("lib_unfused", lib_unfused)):
+    for name, fn in legs:
         g = capture(fn, K)
         ms[name] = timed(g) / K
         del g
     us = {k: round(v * 1e3, 2) for k, v in ms.items()}
     tf = flops / (ms["fused"] * 1e-3) / 1e12
-    tf_base = base_flops / (ms["base"] * 1e-3) / 1e12
-    eprint(f"per call (us): {us}; fused {tf:.0f} TFLOP/s, base GEMM alone {tf_base:.0f} TFLOP/s")
+    tf_base = base_flops / (ms["base"] * 1e-3) / 1e12 if "base" in ms else None
+    eprint(f"per call (us): {us}; fused {tf:.0f} TFLOP/s, base GEMM alone {tf_base} TFLOP/s")
     result = {
         "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill)",
         "value": round(T / (ms["step"] * 1e-3), 1),
@@ -285,11 +287,11 @@ def run_fused_linear(args, torch, L, dev):
             "avg_launch_us": us["fused"],
         },
         "per_call_us": {"fused (shrink + GEMM with the delta in its epilogue)": us["fused"],
-                        "GEMM alone (lora_column_linear)": us["base"],
-                        "GEMM then lora_apply_linear": us["unfused"],
-                        "torch.matmul alone": us["lib_base"],
-                        "torch.matmul then lora_apply_linear": us["lib_unfused"]},
-        "gemm_tflops": round(tf_base, 1),
+                        "GEMM alone (lora_column_linear)": us.get("base"),
+                        "GEMM then lora_apply_linear": us.get("unfused"),
+                        "torch.matmul alone": us.get("lib_base"),
+                        "torch.matmul then lora_apply_linear": us.get("lib_unfused")},
+        "gemm_tflops": None if tf_base is None else round(tf_base, 1),
     }
     print(json.dumps(result), flush=True)
 
@@ -315,6 +317,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="buffer sets (0: enough for >1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="fused_linear: time the fused call only (for profiling its kernels)")
     args = ap.parse_args()
 
     if args.gpus != 1:
