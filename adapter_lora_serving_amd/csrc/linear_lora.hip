@@ -12,18 +12,19 @@
 // shrink / expand kernels: here y = x @ W^T + delta is formed in registers
 // and stored once, so the delta costs no read-modify-write of y.
 //
-// Work: one 256-thread workgroup per 256 x 256 tile of y (256 positions of
-// token_order x 256 output columns); wave (wm, wn) owns 128 x 128 of it as
-// 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 with fp32 accumulators. The
-// product is formed transposed (the W rows are the A operand, the x rows the
-// B operand), so each lane ends with 4 consecutive output columns of one
-// token. Rows are taken in token_order (tokens grouped by slot): x rows are
-// gathered and y rows scattered by token id, and the rows of one tile belong
-// to few slots.
-// Main loop: K in steps of 64; x and W tiles (256 x 64 bf16 each) staged
-// through registers into two LDS buffers (one being read while the next is
-// written), 16-byte chunks stored at chunk ^ (row & 7) so that the MFMA
-// operand reads of 8 consecutive rows hit 8 different bank groups.
+// Work: one 512-thread workgroup (8 waves) per 256 x 256 tile of y (256
+// positions of token_order x 256 output columns); wave (wm, wn) owns 128
+// rows x 64 columns of it as 4 x 8 tiles of v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulators. The product is formed transposed (the W rows are the A
+// operand, the x rows the B operand), so each lane ends with 4 consecutive
+// output columns of one token. Rows are taken in token_order (tokens grouped
+// by slot): x rows are gathered and y rows scattered by token id, and the
+// rows of one tile belong to few slots.
+// Main loop: K in steps of 32 through a ring of 4 LDS stages, each holding
+// the x and W tiles (256 x 32 bf16 each); buffer loads write the ring
+// directly (no registers), three stages ahead of the one being multiplied.
+// The 16-byte chunks of a 64-byte row are stored at chunk ^ ((row >> 1) & 3)
+// so that the operand reads of 16 rows spread over the LDS banks.
 // Epilogue, per slot q with rows in the tile and rank r_q > 0, per 32 ranks:
 // s_q * h of the rows of q (others zero), split into bf16 hi + lo, and the
 // slot's B rows of the tile's columns are staged in LDS, and the delta is
@@ -41,30 +42,16 @@ namespace {
 constexpr int kGT = 256;         // tile rows and columns
 constexpr int kGK = 32;          // K per stage
 constexpr int kStages = 4;       // LDS ring: the stage being read + 3 in flight
-constexpr int kGThreads = 256;
+constexpr int kGThreads = 512;
 constexpr int kStageBytes = kGT * kGK * 2;   // one operand tile of one stage, bf16 (16 KB)
 // LDS: stage s holds [x tile][W tile] at s * 2 * kStageBytes; then token ids
 constexpr int kLdsTok = kStages * 2 * kStageBytes;
 constexpr int kGemmLds = kLdsTok + kGT * 4 + 64;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt operand that waits until at most n vector memory operations are
-// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
-// their maxima, i.e. not waited for)
-constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // D[16x16] += A[16 x 32] . B[16 x 32]^T (v_mfma_f32_16x16x32_bf16): lane
 // (m, g) gives row m, k in [8g, 8g + 8) of both operands and receives
 // D[4g + i][m] in element i.
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// byte offset of 16-byte chunk c of row `row` in a tile of 4 chunks (64 B)
-// per row: chunk c sits at c ^ ((row >> 1) & 3), so the 16-byte MFMA operand
-// reads of 8 consecutive rows (one chunk each) cover all 32 banks once
-__device__ __forceinline__ int swz4(int row, int c) {
-  return row * 64 + ((c ^ ((row >> 1) & 3)) << 4);
 }
 
 }  // namespace
@@ -81,8 +68,8 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
-  const int wm = w >> 1;   // token half of the tile
-  const int wn = w & 1;    // column half
+  const int wm = w >> 2;   // token half of the tile (128 rows)
+  const int wn = w & 3;    // column quarter (64 columns)
   const int m = lane & 15;
   const int g = lane >> 4;
 
@@ -109,7 +96,7 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
 
   // token id of every tile row (position m0 + row of token_order; the
   // identity without an addressing), -1 past T
-  {
+  if (tid < kGT) {
     const int p = m0 + tid;
     tok[tid] = p >= T ? -1 : token_order ? min(max(token_order[p], 0), T - 1) : p;
   }
@@ -123,14 +110,14 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   // of a wave fills a contiguous 1 KB block of LDS, lane L at byte 16 L, i.e.
   // rows 16 blk + L / 4, physical chunk L & 3 of a 64-byte row; the lane
   // fetches the logical chunk stored there (the swizzle is undone on the
-  // global side). Wave w fills blocks w, w + 4, w + 8, w + 12 of both the x
-  // and the W tile of a stage: 8 instructions per wave per stage.
+  // global side). Wave w fills blocks w and w + 8 of both the x and the W
+  // tile of a stage: 4 instructions per wave per stage.
   const int pr = lane >> 2;                          // row within the block
   const int pc = (lane & 3) ^ ((pr >> 1) & 3);       // logical chunk of the lane
-  uint32_t xoff[4], woff[4];
+  uint32_t xoff[2], woff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (w + 4 * j) * 16 + pr;
+  for (int j = 0; j < 2; ++j) {
+    const int row = (w + 8 * j) * 16 + pr;
     const int t = tok[row];
     xoff[j] = t >= 0 ? (uint32_t)t * rowb + (uint32_t)pc * 16u : kOOB;
     woff[j] = n0 + row < out ? (uint32_t)(n0 + row) * rowb + (uint32_t)pc * 16u : kOOB;
@@ -139,20 +126,17 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
     const bool kv = k0 + pc * 8 < in;
     char* sb = lds + (stage % kStages) * 2 * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = w + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x_r, (lds_void*)(sb + blk * 1024), 16,
-          kv && xoff[j] != kOOB ? xoff[j] + (uint32_t)k0 * 2u : kOOB, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_r, (lds_void*)(sb + kStageBytes + blk * 1024), 16,
-          kv && woff[j] != kOOB ? woff[j] + (uint32_t)k0 * 2u : kOOB, 0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      const int blk = w + 8 * j;
+      dma16(x_r, sb + blk * 1024, kv && xoff[j] != kOOB ? xoff[j] + (uint32_t)k0 * 2u : kOOB);
+      dma16(w_r, sb + kStageBytes + blk * 1024,
+            kv && woff[j] != kOOB ? woff[j] + (uint32_t)k0 * 2u : kOOB);
     }
   };
 
-  f32x4 acc[8][8];   // [column tile][token tile]
+  f32x4 acc[4][8];   // [column tile][token tile]
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -160,38 +144,32 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   // three stages in flight before the loop
   for (int st0 = 0; st0 < kStages - 1 && st0 < kt; ++st0) issue(st0, st0 * kGK);
   for (int it = 0; it < kt; ++it) {
-    // this stage's loads are done once at most the later stages' (8 per
+    // this stage's loads are done once at most the later stages' (4 per
     // stage per wave) are outstanding; then the barrier makes every wave's
     // part visible, and frees the buffer read in the previous iteration
     const int ahead = min(kt - 1 - it, kStages - 2);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_le(16));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(8));
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_le(8));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(4));
     else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
-    // a plain s_barrier: __syncthreads()'s release fence would wait for every
-    // load in flight (LDS DMA counts as vector memory) and so empty the ring;
-    // the empty asm statements keep the compiler from moving LDS accesses
-    // across it
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    barrier_no_fence();
     if (it + kStages - 1 < kt) issue(it + kStages - 1, (it + kStages - 1) * kGK);
     const char* xb = lds + (it % kStages) * 2 * kStageBytes;
     const char* wb = xb + kStageBytes;
-    bf16x8 wo[8], xo[8];
+    bf16x8 wo[4], xo[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-      wo[a] = *(const bf16x8*)(wb + swz4(wn * 128 + a * 16 + m, g));
+    for (int a = 0; a < 4; ++a)
+      wo[a] = *(const bf16x8*)(wb + swz4(wn * 64 + a * 16 + m, g));
 #pragma unroll
     for (int a = 0; a < 8; ++a)
       xo[a] = *(const bf16x8*)(xb + swz4(wm * 128 + a * 16 + m, g));
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int bq = 0; bq < 8; ++bq) acc[a][bq] = mfma32(wo[a], xo[bq], acc[a][bq]);
-    // all 16 operand reads first, then the 64 products (each waits only for
-    // its own operands), instead of a full LDS wait before every 8 products
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+    // all 12 operand reads first, then the 32 products (each waits only for
+    // its own operands), instead of a full LDS wait before every few products
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
   }
   __syncthreads();   // the epilogue reuses the ring
 
@@ -221,8 +199,9 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
                                    (uint32_t)out * (uint32_t)R * 2u);
       for (int c0 = 0; c0 < r; c0 += 32) {
         // stage s * h (rows of slot s; zeros elsewhere and past the rank),
-        // split into hi + lo, and B rows of the tile's columns
-        {
+        // split into hi + lo, one token row per thread of the first 256, and
+        // B rows of the tile's columns, one column per thread of the rest
+        if (tid < kGT) {
           const int row = tid;
           const int t = tok[row];
           const bool mine = row >= p0 && row < p1 && t >= 0;
@@ -251,7 +230,9 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
             *(u32x4*)(hb + swz4(row, q)) = hp;
             *(u32x4*)(hl + swz4(row, q)) = lp;
           }
+        } else {
           // B[s, n0 + row, c0 .. c0 + 32): ranks past r read as zero
+          const int row = tid - kGT;
           const int col = n0 + row;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -276,15 +257,15 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
           const char* hsrc = part == 0 ? hb : hl;
-          bf16x8 bo[8], ho[8];
+          bf16x8 bo[4], ho[8];
 #pragma unroll
-          for (int a = 0; a < 8; ++a)
-            bo[a] = *(const bf16x8*)(bb + swz4(wn * 128 + a * 16 + m, g));
+          for (int a = 0; a < 4; ++a)
+            bo[a] = *(const bf16x8*)(bb + swz4(wn * 64 + a * 16 + m, g));
 #pragma unroll
           for (int a = 0; a < 8; ++a)
             ho[a] = *(const bf16x8*)(hsrc + swz4(wm * 128 + a * 16 + m, g));
 #pragma unroll
-          for (int a = 0; a < 8; ++a)
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int bq = 0; bq < 8; ++bq) acc[a][bq] = mfma32(bo[a], ho[bq], acc[a][bq]);
         }
@@ -303,8 +284,8 @@ __global__ __launch_bounds__(kGThreads) void k_linear_lora(
   for (int bq = 0; bq < 8; ++bq) {
     const int t = tok[wm * 128 + bq * 16 + m];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int col = n0 + wn * 128 + a * 16 + 4 * g;
+    for (int a = 0; a < 4; ++a) {
+      const int col = n0 + wn * 64 + a * 16 + 4 * g;
       const f32x4 v = acc[a][bq];
       const uint32_t off = (t >= 0 && col < out) ? ((uint32_t)t * (uint32_t)out + (uint32_t)col) * 2u
                                                  : kOOB;

@@ -304,4 +304,37 @@ __device__ __forceinline__ void bstore16_out(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamOut);
 }
 
+// ---- buffer-to-LDS rings (the SGMV shrink, the base-projection GEMM) ----
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte global -> LDS transfer per lane (buffer_load ... lds): the
+// wave's 64 lanes fill the 1 KB at dst, lane L at byte 16 L. dst must be
+// uniform across the wave. An offset outside the resource writes zeros.
+__device__ __forceinline__ void dma16(rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 0);
+}
+
+// s_waitcnt operand that waits until at most n vector memory operations are
+// outstanding (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for). Transfers into LDS count as vector
+// memory operations.
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Byte offset of logical 16-byte chunk c (0..3) of row `row` in an LDS tile
+// of 64-byte rows: stored at chunk c ^ ((row >> 1) & 3), so that the operand
+// reads of 16 consecutive rows (one chunk each) spread over the banks.
+__device__ __forceinline__ int swz4(int row, int c) {
+  return row * 64 + ((c ^ ((row >> 1) & 3)) << 4);
+}
+
+// Workgroup barrier with no memory fence. __syncthreads()'s release fence
+// waits for every vector memory operation in flight, which would empty a
+// ring of transfers that are meant to stay in flight across it; the empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace lora

@@ -36,6 +36,7 @@
 #include "lora_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace lora {
 
@@ -43,27 +44,32 @@ namespace {
 
 constexpr int kBMe = 64;      // tokens per expand item
 constexpr int kCC = 256;      // output columns per expand item
-constexpr int kKC = 64;       // K elements per staged chunk
-constexpr int kRowB = kKC * 2 + 16;   // padded LDS row (bytes)
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // shrink
 // ---------------------------------------------------------------------------
-// Item: (slot, block of 128 tokens, slice group, K part). Eight waves, wave w
-// owns token tile w (16 tokens) against every rank tile, so its x rows are
-// its own (read into registers D chunks ahead) and only A is shared: A's
-// chunk [RP x 64] goes through a register ring D chunks ahead into a
-// double-buffered LDS tile. A is thus re-read from L2 once per 128 tokens.
-// A slot of rank r uses ntr = ceil(r / 16) rank tiles per slice; a group
-// packs g = min(S, RT / ntr, gmax) slices, slice j of the group on tiles
-// [j * ntr, (j + 1) * ntr). gmax keeps a group's A rows below 2 GiB.
+// Item: (slot, block of 128 tokens, slice group, K part). A slot of rank r
+// uses ntr = ceil(r / 16) rank tiles per slice; a group packs g = min(S,
+// RT / ntr, gmax) slices, slice j of the group on tiles [j * ntr, (j + 1) *
+// ntr), so a slot of small rank reads its x block once for several slices.
+// gmax keeps a group's A rows below 2 GiB.
+// K runs in steps of 32 through a ring of LDS stages, each holding the
+// block's x rows (128 x 32 bf16) and the group's A rows (NT tiles x 16 rows x
+// 32 bf16, NT = the item's live tiles rounded up to a power of two). Buffer
+// loads write the ring directly (no registers), kStages - 1 steps ahead of
+// the step being multiplied, so an item keeps several steps of loads in
+// flight without holding them in registers; rows past the rank, padding
+// tokens and K past `in` arrive as zeros (out-of-range offsets).
+// Eight waves; wave w owns token tile w against the NT rank tiles and skips
+// its products when the tile holds no token. The product is formed as
+// A_rows . x_rows^T, so each lane ends with 4 consecutive ranks of one token
+// and stores them as one 16-byte vector.
 // With kparts > 1 each item writes its partial h to its own buffer
 // (hout + kp * part_stride); k_sum_parts adds them in kp order. Every item
 // writes the columns of its slices below 16 * ntr.
 constexpr int kBMs = 128;
-constexpr int kD = 4;
 
 // Slices per item for a slot of rank r (r > 0) in a kernel of RT rank tiles.
 __device__ __forceinline__ int shrink_group(int r, int RT, int S, int gmax) {
@@ -71,31 +77,47 @@ __device__ __forceinline__ int shrink_group(int r, int RT, int S, int gmax) {
   return max(1, min(min(S, RT / ntr), gmax));
 }
 
+// LDS ring of the shrink (dynamic shared memory). A stage covers KS
+// elements of K: 128 B rows up to 4 rank tiles, so that x is read in whole
+// 128-byte lines; 64 B rows above, where a deeper stage would leave room for
+// one workgroup per CU. Stage s at s * kStage: [x rows: 128 x RB][A rows: RT
+// * 16 x RB]; then a 1 KB landing block for the empty transfers of waves with
+// no A rows to load.
 template <int RT>
-// Six waves per SIMD (three workgroups per CU) keep a prefill batch's items
-// resident in one round, so no item starts after the first round ends; at 16
-// rank tiles the LDS allows two workgroups per CU, so four waves per SIMD
-// (128 VGPRs) are enough and keep the accumulators in registers.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 4 : 6))) void k_sgmv_shrink(
+struct ShrinkRing {
+  static constexpr int KS = RT <= 4 ? 64 : 32;   // K elements per stage
+  static constexpr int RB = KS * 2;              // bytes per row
+  static constexpr int CH = RB / 16;             // 16-byte chunks per row
+  static constexpr int RPB = 1024 / RB;          // rows per 1 KB transfer block
+  static constexpr int kX = kBMs * RB;
+  static constexpr int kA = RT * 16 * RB;
+  static constexpr int kStage = kX + kA;
+  // stages: as many as leave room for two workgroups per CU
+  static constexpr int kStages = (RT == 1 || RT == 8) ? 4 : 3;
+  static constexpr int kFill = kStages * kStage;
+  static constexpr int kBytes = kFill + 1024;
+  // byte offset of logical chunk c of row `row` in a tile: rows of 4 chunks
+  // store chunk c at c ^ ((row >> 1) & 3), rows of 8 at c ^ (row & 7), so
+  // that the operand reads of 16 consecutive rows spread over the banks
+  static __device__ __forceinline__ int swz(int row, int c) {
+    if constexpr (CH == 4) return swz4(row, c);
+    return row * 128 + ((c ^ (row & 7)) << 4);
+  }
+};
+
+template <int RT>
+// two workgroups per CU (the ring's LDS)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_sgmv_shrink(
     const void* __restrict__ x_, int T, int in, const void* __restrict__ a_, int slots, int S,
     int R, const int32_t* __restrict__ order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, float* __restrict__ hout, int kparts,
     int64_t part_stride, int min_len, int gmax) {
-  constexpr int RP = RT * 16;
-  constexpr int AL = RP >= 64 ? RP / 64 : 1;   // A pieces per thread per chunk
-  // chunks in flight: 2 from 4 rank tiles up (measured at 4: prefill down
-  // 106 -> 101 us against 3; at 8 a third chunk more than doubled the skewed
-  // mix's time)
-  constexpr int D = RT >= 4 ? 2 : kD;
-  // XL: x rows are loaded as 8 rows x 128 contiguous bytes per instruction
-  // and turned into the MFMA operand layout through a per-wave LDS tile
-  // (16 rows x 64 bytes per instruction otherwise); the tile's 18 KB would
-  // cost a workgroup per CU at the largest ranks, so those load directly
-  constexpr bool XL = RT <= 4;
+  using Ring = ShrinkRing<RT>;
+  constexpr int KS = Ring::KS;
+  constexpr int CH = Ring::CH;
+  extern __shared__ __attribute__((aligned(16))) char ring[];
   __shared__ int scratch[24];
   __shared__ int tok[kBMs];
-  __shared__ __attribute__((aligned(16))) char as[2][RP * kRowB];
-  __shared__ __attribute__((aligned(16))) char xs[XL ? 8 : 1][XL ? 16 * kRowB : 16];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -129,161 +151,131 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(RT >= 16 ? 
   const int gsz = min(g, S - i0);   // slices in the group
   const int live = gsz * ntr;       // rank tiles holding rows below r
   const int ntok = min(kBMs, n - mb * kBMs);
-  // the token ids are the oldest loads in flight; the first A chunks (which
-  // do not depend on them) are issued next, then the ids are waited for
-  const int tv = token_at(order, seg0 + mb * kBMs + min(tid, ntok - 1), T);
+  if (tid < kBMs) tok[tid] = tid < ntok ? token_at(order, seg0 + mb * kBMs + tid, T) : -1;
+  __syncthreads();
 
   const rsrc_t x_r = make_rsrc(x_, (uint32_t)T * (uint32_t)in * 2u);
   // the group's A rows: slices i0 .. i0 + gsz - 1 of the slot
   const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * S + i0) * R * in * 2,
                                (uint32_t)gsz * (uint32_t)R * (uint32_t)in * 2u);
   const uint32_t rowG = (uint32_t)in * 2u;
-  const int nchT = (in + kKC - 1) / kKC;
-  const int cbeg = (int)((int64_t)nchT * kp / kparts);
-  const int cend = (int)((int64_t)nchT * (kp + 1) / kparts);
-  const int nch = cend - cbeg;
+  const int steps = (in + KS - 1) / KS;
+  const int s0 = (int)((int64_t)steps * kp / kparts);
+  const int nst = (int)((int64_t)steps * (kp + 1) / kparts) - s0;
 
-  const int m = lane & 15;
-  const int kg = lane >> 4;
-  const int arow = tid >> 3;        // 0..63 (+64 per extra piece)
-  const int apc = tid & 7;
-  // LDS tile row v holds row v % (16 ntr) of slice v / (16 ntr) of the group
-  uint32_t abase[AL];
+  // Transfers: one instruction of a wave fills a 1 KB block of a stage, RPB
+  // rows, lane L at byte 16 L (row L / CH, physical chunk L % CH); the lane
+  // fetches the logical chunk stored there (the swizzle is undone on the
+  // global side). Wave w fills x blocks w (+ 8) and A blocks w (+ 8 j); a
+  // wave past the item's A blocks sends an empty transfer to the landing
+  // block, so every wave counts the same transfers per stage.
+  constexpr int XB = kBMs / Ring::RPB / 8;   // x blocks per wave per stage
+  const int pr = lane / CH;
+  const int pc = CH == 4 ? (lane & 3) ^ ((pr >> 1) & 3) : (lane & 7) ^ (pr & 7);
+  uint32_t xoff[XB];
 #pragma unroll
-  for (int q = 0; q < AL; ++q) {
-    const int v = arow + 64 * q;
+  for (int j = 0; j < XB; ++j) {
+    const int xt = tok[(w + 8 * j) * Ring::RPB + pr];
+    xoff[j] = xt >= 0 ? (uint32_t)xt * rowG + (uint32_t)pc * 16u : kOOB;
+  }
+  auto a_off = [&](int blk) -> uint32_t {
+    const int v = blk * Ring::RPB + pr;
     const int j = v / (16 * ntr);
     const int rr = v - j * 16 * ntr;
-    abase[q] = (v < RP && j < gsz && rr < r) ? (uint32_t)(j * R + rr) * rowG : kOOB;
-  }
-
-  u32x4 xr[D][2];
-  u32x4 ar[D][AL];
-  auto issue_a = [&](int slot, int c) {   // A loads of chunk c (relative) into ring slot
-    const bool cv = c < nch;
-    const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
-#pragma unroll
-    for (int q = 0; q < AL; ++q) {
-      const uint32_t e = (uint32_t)((cbeg + c) * kKC + apc * 8);
-      ar[slot][q] = bload16(a_r, (cv && abase[q] != kOOB && e < (uint32_t)in)
-                                     ? abase[q] + kb + apc * 16u
-                                     : kOOB);
-    }
+    return (j < gsz && rr < r) ? (uint32_t)(j * R + rr) * rowG + (uint32_t)pc * 16u : kOOB;
   };
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue_a(d, d);
-  if (tid < kBMs) tok[tid] = tid < ntok ? tv : -1;
-  __syncthreads();
-  // x rows of this lane: XL: rows xq and xq + 8 of the wave's 16 tokens,
-  // 16-byte piece xp of the chunk; else row m, pieces kg and 4 + kg
-  const int xq = lane >> 3;
-  const int xp = lane & 7;
-  uint32_t xrow[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int t = tok[w * 16 + (XL ? xq + 8 * hh : m)];
-    xrow[hh] = t >= 0 ? (uint32_t)t * rowG : kOOB;
-  }
-  auto issue_x = [&](int slot, int c) {   // x loads of chunk c (relative) into ring slot
-    const bool cv = c < nch;
-    const uint32_t kb = (uint32_t)(cbeg + c) * (kKC * 2u);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int ke = XL ? xp * 8 : hh * 32 + kg * 8;   // element offset in the chunk
-      const uint32_t e = (uint32_t)((cbeg + c) * kKC + ke);
-      xr[slot][hh] = bload16(x_r, (cv && xrow[hh] != kOOB && e < (uint32_t)in)
-                                      ? xrow[hh] + kb + (uint32_t)ke * 2u
-                                      : kOOB);
-    }
-  };
-  auto stage = [&](int slot, int buf) {   // A chunk in ring slot -> LDS buffer
-#pragma unroll
-    for (int q = 0; q < AL; ++q) {
-      const int row = arow + 64 * q;
-      if (row < RP) *(u32x4*)(as[buf] + row * kRowB + apc * 16) = ar[slot][q];
-    }
-  };
+  const bool prod = w * 16 < ntok;   // this wave's token tile holds tokens
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+  const int SR = S * R;
+  float* hp = hout + (int64_t)kp * part_stride;
 
   f32x4 acc[RT];
 #pragma unroll
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the K loop and the store for NT rank tiles (a compile-time count)
+  auto run = [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    constexpr int NAB = NT * 16 / Ring::RPB;     // A blocks per stage
+    constexpr int AB = NAB >= 8 ? NAB / 8 : 1;   // A transfers per wave per stage
+    constexpr int LW = XB + AB;                  // transfers per wave per stage
+    uint32_t aoff[AB];
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue_x(d, d);
-  stage(0, 0);
-  __syncthreads();
-#pragma unroll 1
-  for (int c0 = 0; c0 < nch; c0 += D) {
+    for (int j = 0; j < AB; ++j) aoff[j] = a_off(w + 8 * j);
+    auto issue = [&](int st) {
+      char* sb = ring + (st % Ring::kStages) * Ring::kStage;
+      const uint32_t kb = (uint32_t)(s0 + st) * (uint32_t)Ring::RB;   // the step's bytes in a row
+      const bool kv = (s0 + st) * KS + pc * 8 < in;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int c = c0 + d;
-      if (c < nch) {
-        if (c + 1 < nch) stage((d + 1) % D, (c + 1) & 1);
-        const char* ab = as[c & 1];
-        if constexpr (XL) {
-          *(u32x4*)(xs[w] + xq * kRowB + xp * 16) = xr[d][0];
-          *(u32x4*)(xs[w] + (xq + 8) * kRowB + xp * 16) = xr[d][1];
-          __builtin_amdgcn_wave_barrier();
-        }
+      for (int j = 0; j < XB; ++j)
+        dma16(x_r, sb + (w + 8 * j) * 1024, kv && xoff[j] != kOOB ? xoff[j] + kb : kOOB);
+      if constexpr (NAB >= 8) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 xa;
-          if constexpr (XL)
-            xa = __builtin_bit_cast(bf16x8,
-                                    *(const u32x4*)(xs[w] + m * kRowB + (ks * 32 + kg * 8) * 2));
-          else
-            xa = __builtin_bit_cast(bf16x8, xr[d][ks]);
+        for (int j = 0; j < AB; ++j)
+          dma16(a_r, sb + Ring::kX + (w + 8 * j) * 1024,
+                kv && aoff[j] != kOOB ? aoff[j] + kb : kOOB);
+      } else {
+        char* dst = w < NAB ? sb + Ring::kX + w * 1024 : ring + Ring::kFill;
+        dma16(a_r, dst, (w < NAB && kv && aoff[0] != kOOB) ? aoff[0] + kb : kOOB);
+      }
+    };
+    for (int st = 0; st < Ring::kStages - 1 && st < nst; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // this step's transfers are done once at most the later steps' are
+      // outstanding; the barrier then makes every wave's transfers visible
+      // and frees the buffer read in the previous step
+      const int ahead = min(nst - 1 - st, Ring::kStages - 2);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LW));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le(LW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+      barrier_no_fence();
+      if (st + Ring::kStages - 1 < nst) issue(st + Ring::kStages - 1);
+      if (prod) {
+        const char* sb = ring + (st % Ring::kStages) * Ring::kStage;
 #pragma unroll
-          for (int nt = 0; nt < RT; ++nt) {
-            // tiles past the group's rows hold only zeros (16 tiles take a
-            // guard instead of an early exit, so that the loop unrolls)
-            if (RT < 16 && nt >= live) break;
-            if (nt < live) {
-              const bf16x8 av = __builtin_bit_cast(
-                  bf16x8, *(const u32x4*)(ab + (nt * 16 + m) * kRowB + (ks * 32 + kg * 8) * 2));
-              acc[nt] = mfma_k32(xa, av, acc[nt]);
-            }
+        for (int h = 0; h < KS / 32; ++h) {   // 32-element MFMA steps of the stage
+          const int c = 4 * h + kg;            // the lane's logical chunk
+          const bf16x8 xo = *(const bf16x8*)(sb + Ring::swz(w * 16 + m, c));
+          // tiles in groups of 8: all reads of a group, then its products
+#pragma unroll
+          for (int n0 = 0; n0 < NT; n0 += 8) {
+            constexpr int NG = NT < 8 ? NT : 8;
+            bf16x8 ao[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+              ao[q] = *(const bf16x8*)(sb + Ring::kX + Ring::swz((n0 + q) * 16 + m, c));
+#pragma unroll
+            for (int q = 0; q < NG; ++q) acc[n0 + q] = mfma_k32(ao[q], xo, acc[n0 + q]);
           }
         }
-        issue_a(d, c + D);
-        issue_x(d, c + D);
-        __syncthreads();
       }
     }
-  }
-
-  // lane (m, kg) holds h[token w*16 + 4kg + ii][slice i0 + nt / ntr, rank
-  // (nt % ntr) * 16 + m]
-  const int SR = S * R;
-  float* hp = hout + (int64_t)kp * part_stride;
-  if constexpr (RT < 16) {
+    // lane (m, kg) holds h[token tile w, row m][tile nt, ranks 4 kg .. 4 kg + 3]
+    const int t = tok[w * 16 + m];
+    if (!prod || t < 0) return;
 #pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      if (nt >= live) break;
+    for (int nt = 0; nt < NT; ++nt) {
       const int j = nt / ntr;
-      const int rr = (nt - j * ntr) * 16 + m;
-      if (rr < R) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int tt = tok[w * 16 + 4 * kg + ii];
-          if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + rr] = acc[nt][ii];
-        }
-      }
+      const int rr = (nt - j * ntr) * 16 + 4 * kg;
+      if (nt < live && rr < R)
+        *(f32x4*)(hp + (int64_t)t * SR + (i0 + j) * R + rr) = acc[nt];
     }
-  } else {   // 16 tiles: no early exit, so that the loop unrolls
-    int j = 0, rt = 0;   // slice in the group and rank tile of tile nt
-#pragma unroll
-    for (int nt = 0; nt < RT; ++nt) {
-      const int rr = rt * 16 + m;
-      if (nt < live && rr < R) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int tt = tok[w * 16 + 4 * kg + ii];
-          if (tt >= 0) hp[(int64_t)tt * SR + (i0 + j) * R + rr] = acc[nt][ii];
-        }
-      }
-      if (++rt == ntr) { rt = 0; ++j; }
-    }
+  };
+  const int ntp = live <= 1 ? 1 : live <= 2 ? 2 : live <= 4 ? 4 : live <= 8 ? 8 : 16;
+  if constexpr (RT >= 16) {
+    if (ntp == 16) return run(std::integral_constant<int, 16>{});
   }
+  if constexpr (RT >= 8) {
+    if (ntp == 8) return run(std::integral_constant<int, 8>{});
+  }
+  if constexpr (RT >= 4) {
+    if (ntp == 4) return run(std::integral_constant<int, 4>{});
+  }
+  if constexpr (RT >= 2) {
+    if (ntp == 2) return run(std::integral_constant<int, 2>{});
+  }
+  run(std::integral_constant<int, 1>{});
   // columns [16 ntr, R) of each slice are not written: lora_shrink's VALU
   // kernel writes the zeros of h, and lora_apply_linear's h is read only
   // below the rank
@@ -655,8 +647,17 @@ hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int s
   const int gmax = (int)std::max<int64_t>(1, std::min<int64_t>(S, (((int64_t)1 << 31) - 1) /
                                                                        slice_bytes));
 #define L(RTV)                                                                                 \
-  hipLaunchKernelGGL(k_sgmv_shrink<RTV>, dim3((unsigned)grid), dim3(512), 0, stream, x, T, in, \
-                     a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len, gmax)
+  do {                                                                                         \
+    constexpr int lds = ShrinkRing<RTV>::kBytes;                                               \
+    if (lds > 65536) {                                                                         \
+      const hipError_t e = hipFuncSetAttribute((const void*)k_sgmv_shrink<RTV>,                \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds); \
+      if (e != hipSuccess) return e;                                                           \
+    }                                                                                          \
+    hipLaunchKernelGGL(k_sgmv_shrink<RTV>, dim3((unsigned)grid), dim3(512), lds, stream, x, T, \
+                       in, a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len, \
+                       gmax);                                                                  \
+  } while (0)
   switch (rt_of(R)) {
     case 1: L(1); break;
     case 2: L(2); break;
