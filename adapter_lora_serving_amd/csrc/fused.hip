@@ -874,29 +874,41 @@ int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-int decode_chunk_cols(int R) {
-  // columns per decode expand piece; overridable for tuning experiments
+int decode_chunk_cols(int R, int out, int slots) {
+  // columns per decode expand piece: 1024 up to rank 32, else 2048; twice
+  // that when a batch of many slots would otherwise make more than 4096
+  // expand pieces, whose fixed cost (ticket, token ids, wait) then dominates
+  // (measured on the routed-expert gate/up, 256 pool entries x 28672
+  // outputs: 103.6 -> 93.5 us; the 32-slot qkv decode keeps 1024);
+  // overridable for tuning experiments
   const int env = env_int("LORA_DECODE_CHUNK", 0);
   if (env >= 16 && env % 16 == 0) return env;
-  return R <= 32 ? 1024 : 2048;
+  int cols = R <= 32 ? 1024 : 2048;
+  if ((int64_t)slots * ((out + cols - 1) / cols) > 4096) cols *= 2;
+  return cols;
 }
 
-int k_parts(int in, int out) {
+int k_parts(int in, int out, int slots, int S) {
   // K parts of a decode shrink: ~2048 deep, or ~1024 when the output is
   // narrower than one expand chunk (a router's logits: then every slot has a
   // single expand piece, and more, shorter shrink pieces shorten the chain:
   // measured at 64 outputs, 9.5 -> 8.1 us for 2 -> 4 parts; 8 parts 9.4 us);
-  // overridable for tuning
+  // then fewer while the shrink pieces (slots x slices x parts) would number
+  // more than 1024 (the routed-expert down product, 256 pool entries, in
+  // 14336: 7 parts 41.1 us, 4 parts 39.0 us); overridable for tuning
   const int env = env_int("LORA_KPARTS", 0);
   int kp = env > 0 ? env : in / (out < 1024 ? 1024 : 2048);
-  return kp < 1 ? 1 : kp > 8 ? 8 : kp;
+  kp = kp < 1 ? 1 : kp > 8 ? 8 : kp;
+  if (env <= 0)
+    while (kp > 1 && (int64_t)slots * S * kp > 1024) --kp;
+  return kp;
 }
 
 // Expand chunks: each slice cut into pieces of at most `cols` columns (a
 // multiple of 16), at most kMaxChunks in all.
-ChunkTable make_chunks(const SliceTable& st, int R) {
+ChunkTable make_chunks(const SliceTable& st, int R, int slots) {
   ChunkTable ct;
-  int cols = decode_chunk_cols(R);
+  int cols = decode_chunk_cols(R, st.off[st.n], slots);
   for (;;) {
     int n = 0;
     for (int i = 0; i < st.n; ++i) {
@@ -937,7 +949,7 @@ size_t fused_partial_bytes(int slots, int S, int R, int in) {
   const int RP = rt_bucket(R) * 16;
   // room for the most parts any output width takes; 8 bytes per entry
   // (value and tag)
-  return (size_t)slots * S * k_parts(in, 0) * kMT * RP * sizeof(uint64_t);
+  return (size_t)slots * S * k_parts(in, 0, 1, 1) * kMT * RP * sizeof(uint64_t);
 }
 
 bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in) {
@@ -960,8 +972,8 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const int32_t* ranks, const float* scalings, void* workspace,
                               hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const ChunkTable ct = make_chunks(st, R);
-  const int KP = k_parts(in, st.off[st.n]);
+  const ChunkTable ct = make_chunks(st, R, slots);
+  const int KP = k_parts(in, st.off[st.n], slots, st.n);
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
   // rank classes (largest first) where ranks differ enough to matter
   const int nclass = rt_bucket(R) >= 4 ? 3 : 1;
@@ -1035,7 +1047,7 @@ hipError_t launch_decode_expand(void* y, int T, const SliceTable& st, const floa
                                 const int32_t* indptr, const int32_t* ranks,
                                 const float* scalings, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const ChunkTable ct = make_chunks(st, R);
+  const ChunkTable ct = make_chunks(st, R, slots);
   const int64_t grid = 8 * (int64_t)((slots + 7) / 8) * ct.n;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const int rt = rt_bucket(R);

@@ -164,11 +164,19 @@ size_t lora_shrink_workspace_bytes(int64_t T, int64_t in_features, int32_t num_s
   return kp > 1 ? ws_h_bytes(T, num_slices, R) * kp : 0;
 }
 
-lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features, const void* a,
+}  // extern "C"
+
+namespace {
+
+// lora_shrink's body. zeros: whether the columns of h that no expand reads
+// (past each slot's rank, rows of dead tokens and rank-0 slots) are written
+// as zeros, as lora_shrink promises its callers; an internal h that only
+// the fused GEMM's epilogue reads (below each slot's rank) skips them.
+lora_status shrink_impl(int dtype, const void* x, int64_t T, int64_t in_features, const void* a,
                         int32_t slots, int32_t num_slices, int32_t R,
                         const int32_t* token_order, const int32_t* slot_indptr,
                         const int32_t* ranks, float* h, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool zeros) {
   lora_status st = check_common(dtype, T, slots, R);
   if (st != LORA_OK) return st;
   if (num_slices < 1 || num_slices > lora::kMaxSlices) return LORA_ERR_UNSUPPORTED;
@@ -194,9 +202,10 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
   // do not take) the VALU kernel computes every segment.
   const bool mfma = shrink_on_mfma(dtype, T, in_features, num_slices, R);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                     token_order, slot_indptr, ranks, h,
-                                     mfma ? 0 : lora::kNoMaxSeg, s);
+  hipError_t e = hipSuccess;
+  if (!mfma || zeros)
+    e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
+                            token_order, slot_indptr, ranks, h, mfma ? 0 : lora::kNoMaxSeg, s);
   const bool large = T >= kLargeBatch;
   if (e == hipSuccess && mfma && !large)
     e = lora::launch_decode_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
@@ -207,6 +216,19 @@ lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features
                                  kparts > 1 ? static_cast<float*>(workspace) : nullptr, kparts,
                                  large ? 0 : lora::kLongSegment, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status lora_shrink(int dtype, const void* x, int64_t T, int64_t in_features, const void* a,
+                        int32_t slots, int32_t num_slices, int32_t R,
+                        const int32_t* token_order, const int32_t* slot_indptr,
+                        const int32_t* ranks, float* h, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return shrink_impl(dtype, x, T, in_features, a, slots, num_slices, R, token_order, slot_indptr,
+                     ranks, h, workspace, workspace_bytes, stream, true);
 }
 
 lora_status lora_gather_shrink(int dtype, const int32_t* ids, int64_t T, int64_t vocab,
@@ -313,13 +335,15 @@ lora_status lora_fused_column_linear(int dtype, const void* x, const void* w, vo
   const size_t need = lora_fused_column_linear_workspace_bytes(T, in_features, num_slices, R);
   if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
-  // h of every token (zeros where the expand does not read), then the base
-  // projection with the delta of h in its epilogue
+  // h of the adapted tokens (below each slot's rank: the only columns the
+  // epilogue uses), then the base projection with the delta of h in its
+  // epilogue
   float* h = static_cast<float*>(workspace);
   const size_t hb = ws_h_bytes(T, num_slices, R);
   const size_t pb = workspace_bytes - hb;
-  st = lora_shrink(dtype, x, T, in_features, a, slots, num_slices, R, token_order, slot_indptr,
-                   ranks, h, pb > 0 ? static_cast<char*>(workspace) + hb : nullptr, pb, stream);
+  st = shrink_impl(dtype, x, T, in_features, a, slots, num_slices, R, token_order, slot_indptr,
+                   ranks, h, pb > 0 ? static_cast<char*>(workspace) + hb : nullptr, pb, stream,
+                   false);
   if (st != LORA_OK) return st;
   return hip_status(lora::launch_linear_lora(x, w, y, (int)T, (int)in_features, tab, h, b, slots,
                                              R, token_order, slot_indptr, ranks, scalings,

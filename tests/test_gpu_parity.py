@@ -385,6 +385,10 @@ EDGE = {
     # per item for the small ranks
     "large_rank256": dict(T=1100, in_f=648, out_slices=(256, 96, 32), R=256, slots=6,
                           ranks=[256, 200, 17, 0, 128, 48], dead=0.02),
+    # one rank tile on the SGMV tiles (a single A block per K step, most
+    # waves sending empty transfers), `in` not a multiple of the step
+    "large_rank16": dict(T=1300, in_f=1064, out_slices=(384, 128), R=16, slots=20,
+                         ranks=[16, 8, 3, 0, 12] * 4, skew=1.2, dead=0.03),
 }
 
 
