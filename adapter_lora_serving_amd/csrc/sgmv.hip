@@ -10,14 +10,14 @@
 // layout follows mstar.model.components.linear, FusedColumnLinear.
 //
 // Shrink item: (slot, block of 128 tokens of its segment, slice group, K
-//   part). Eight waves; wave w owns token tile w against every rank tile.
-//   Its x rows go straight from HBM into registers a few 64-element chunks
-//   ahead; A's chunk is shared through a double-buffered LDS tile. A slot
-//   whose rank needs fewer rank tiles than the kernel holds takes several
-//   slices in one item (their tiles side by side), so its x block is read
-//   once for all of them. Rows of A at or past the rank read as zeros
-//   without a memory access. With several K parts each item writes a
-//   partial h and a second kernel sums the parts.
+//   part). Eight waves; wave w owns token tile w against the item's rank
+//   tiles. The x block and the A rows stream through a ring of LDS stages
+//   that buffer-to-LDS loads fill a few K steps ahead. A slot whose rank
+//   needs fewer rank tiles than the kernel holds takes several slices in one
+//   item (their tiles side by side), so its x block is read once for all of
+//   them. Rows of A at or past the rank read as zeros without a memory
+//   access. With several K parts each item writes a partial h and a second
+//   kernel sums the parts.
 // Expand item: (slot, block of 64 tokens, 256 output columns of one slice).
 //   The block's h rows are scaled and split into bf16 hi + lo in LDS; every
 //   wave prefetches its 4 column tiles of B and y in one round trip, then
