@@ -631,65 +631,6 @@ int sgmv_kparts(int in) {
   return kp < 1 ? 1 : kp > 16 ? 16 : kp;
 }
 
-namespace {
-
-// Workgroups of the shrink for rank bucket RT resident at once on the
-// current device (its ring is dynamic LDS); 0 if the runtime cannot say.
-template <int RT>
-int64_t shrink_resident() {
-  constexpr int lds = ShrinkRing<RT>::kBytes;
-  if (lds > 65536 && hipFuncSetAttribute((const void*)k_sgmv_shrink<RT>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         lds) != hipSuccess)
-    return 0;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_sgmv_shrink<RT>, 512, lds) !=
-          hipSuccess)
-    return 0;
-  return (int64_t)cus * per_cu;
-}
-
-}  // namespace
-
-int sgmv_kparts_for(int T, int in, int S, int R) {
-  // At most sgmv_kparts(in) parts (what the workspace is sized for), and of
-  // those the count whose items best fill whole rounds of resident
-  // workgroups, estimating the items as slice groups x parts x 128-token
-  // blocks (segments of whole blocks); a tie keeps more parts. Measured on
-  // the prefill down product (T 8192, in 14336, 64 blocks): 8 parts (one
-  // round of 512) 92.6 us, 14 parts (1.75 rounds) 96.3 us, 10 parts 98.4
-  // us; the other workloads keep sgmv_kparts(in).
-  const int kp0 = sgmv_kparts(in);
-  if (kp0 <= 1 || T <= 0) return kp0;
-  const int rt = rt_of(R);
-  int64_t res = 0;
-  switch (rt) {
-    case 1: res = shrink_resident<1>(); break;
-    case 2: res = shrink_resident<2>(); break;
-    case 4: res = shrink_resident<4>(); break;
-    case 8: res = shrink_resident<8>(); break;
-    default: res = shrink_resident<16>(); break;
-  }
-  if (res <= 0) return kp0;
-  const int ntr = (R + 15) / 16;
-  const int g = std::max(1, std::min(S, rt / ntr));
-  const int64_t per_part = (int64_t)((S + g - 1) / g) * ((T + kBMs - 1) / kBMs);
-  int best = kp0;
-  double best_fill = -1.0;
-  for (int kp = kp0; kp >= 1; --kp) {
-    const int64_t items = per_part * kp;
-    const int64_t rounds = (items + res - 1) / res;
-    const double fill = (double)items / (double)(rounds * res);
-    if (fill > best_fill + 1e-9) {
-      best_fill = fill;
-      best = kp;
-    }
-  }
-  return best;
-}
-
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
                               int R, const int32_t* order, const int32_t* indptr,
                               const int32_t* ranks, float* h, float* parts, int kparts,
