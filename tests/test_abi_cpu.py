@@ -136,6 +136,45 @@ def test_apply_linear_validation_and_workspace(lib):
     assert call(T=0, ws=None) == OK
 
 
+def test_column_linear_validation(lib):
+    """The base projection and the fused-epilogue call refuse bad host
+    arguments before any launch: fp32, a slice width that is not a multiple
+    of 256, `in` not a multiple of 8, a buffer of 2 GiB or more, null or
+    misaligned pointers, a short or misaligned workspace."""
+    f = lib.lora_column_linear
+    sl = _slices(512, 256)
+    assert f(0, A16, A16, A16, 300, 512, sl, 2, None) == UNSUPPORTED
+    assert f(1, A16, A16, A16, 300, 512, _slices(504), 1, None) == UNSUPPORTED
+    assert f(1, A16, A16, A16, 300, 512, _slices(500), 1, None) == ALIGN      # not 8-element rows
+    assert f(1, A16, A16, A16, 300, 516, sl, 2, None) == UNSUPPORTED
+    assert f(1, A16, A16, A16, 1 << 20, 512, _slices(1024), 1, None) == UNSUPPORTED   # y of 2 GiB
+    assert f(1, A16, A16, A16, -1, 512, sl, 2, None) == INVALID
+    assert f(1, None, A16, A16, 300, 512, sl, 2, None) == INVALID
+    assert f(1, MIS, A16, A16, 300, 512, sl, 2, None) == ALIGN
+    assert f(1, None, None, None, 0, 512, sl, 2, None) == OK      # nothing to do
+
+    g = lib.lora_fused_column_linear
+    need = lib.lora_fused_column_linear_workspace_bytes(300, 512, 2, 16)
+    assert need >= 300 * 2 * 16 * 4
+    assert lib.lora_fused_column_linear_workspace_bytes(-1, 512, 2, 16) == 0
+
+    def call(dtype=1, x=A16, T=300, inf=512, widths=(512, 256), R=16, order=A16, ws=A16,
+             nbytes=need):
+        return g(dtype, x, A16, A16, T, inf, _slices(*widths), len(widths), A16, A16, 8, R,
+                 order, A16, A16, A16, ws, nbytes, None)
+
+    assert call(dtype=0) == UNSUPPORTED
+    assert call(widths=(504,)) == UNSUPPORTED
+    assert call(inf=516) == UNSUPPORTED
+    assert call(R=0) == UNSUPPORTED
+    assert call(x=None) == INVALID
+    assert call(order=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(ws=A16 + 16) == ALIGN             # workspace must be 256-byte aligned
+    assert call(T=0, ws=None) == OK
+
+
 def test_addressing_validation(lib):
     f = lib.lora_build_addressing
     assert f(A16, -1, 4, A16, A16, None, 0, None) == INVALID
