@@ -125,3 +125,60 @@ def test_fused_column_linear_prefill_full_sampled():
     pick.update(np.random.default_rng(4).choice(wl.T, size=40, replace=False).tolist())
     idx = np.array(sorted(pick))
     assert_tol(y[idx], _reference(wl, tg, w, rows=idx), "full prefill gate/up")
+
+
+def test_fused_column_linear_graph_equals_eager():
+    """The addressing build and the fused call recorded in one hipGraph
+    (a batch over 1024 tokens, so the shrink's K parts live in the
+    workspace), replayed with new x and new token slots: every replay equals
+    eager execution on the same inputs bit for bit, and two eager calls are
+    bit-identical."""
+    t = torch()
+    wl = W.make_config(3, 4, T=1100, in_features=512, inter=768)
+    tg = wl.target("gate_up")
+    w = dev(W.base_weight(wl, tg), "bf16")
+    g = GpuTarget(wl, tg)
+    T, out = wl.T, sum(tg.out_slices)
+    ts = g.token_slot.clone()
+    x = g.x.clone()
+    addr = L.build_addressing(ts, wl.slots)
+    y = t.empty(T, out, dtype=t.bfloat16, device="cuda:0")
+    need = int(L.lib().lora_fused_column_linear_workspace_bytes(T, tg.in_features,
+                                                               tg.num_slices, wl.R))
+    ws = t.empty(need, dtype=t.uint8, device="cuda:0")
+
+    def step():
+        L.build_addressing(ts, wl.slots, out=addr)
+        L.fused_column_linear(x, w, g.a, g.b, addr, g.ranks, g.scal, tg.out_slices, y=y,
+                              workspace=ws)
+
+    step()
+    t.cuda.synchronize()
+    y_first = y.clone()
+    step()
+    t.cuda.synchronize()
+    assert t.equal(y, y_first), "two eager calls differ"
+
+    graph = t.cuda.CUDAGraph()
+    st = t.cuda.Stream()
+    with t.cuda.stream(st):
+        with t.cuda.graph(graph, stream=st):
+            step()
+    t.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    for rep in range(3):
+        log(f"fused linear graph replay {rep}")
+        new_x = W.f32_to_bf16_bits(rng.standard_normal((T, tg.in_features), dtype=np.float32))
+        new_ts = rng.integers(-1, wl.slots, size=T).astype(np.int32)
+        x.copy_(dev(new_x, "bf16"))
+        ts.copy_(t.from_numpy(new_ts))
+        t.cuda.synchronize()
+        graph.replay()
+        t.cuda.synchronize()
+        y_graph = y.clone()
+        a_e = L.build_addressing(t.from_numpy(new_ts).to("cuda:0"), wl.slots)
+        y_e = L.fused_column_linear(dev(new_x, "bf16"), w, g.a, g.b, a_e, g.ranks, g.scal,
+                                    tg.out_slices)
+        t.cuda.synchronize()
+        assert t.equal(addr.token_order, a_e.token_order)
+        assert t.equal(y_graph, y_e), f"replay {rep}"
