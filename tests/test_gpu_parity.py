@@ -408,6 +408,45 @@ def test_edge_cases(case, fused):
     assert np.array_equal(f64(y)[same], O.decode(tg.y0, wl.dtype)[same])
 
 
+def _random_shape(seed):
+    """A seeded random batch: sizes, slices, ranks, dead tokens and skew all
+    drawn, spanning the small-batch fused kernel (T < 1024) and the
+    segment-tiled kernels (T >= 1024); widths that are not multiples of 16
+    take the VALU kernels."""
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.choice([int(rng.integers(1, 1024)), int(rng.integers(1024, 2200))]))
+    in_f = 8 * int(rng.integers(1, 129))
+    S = int(rng.integers(1, 5))
+    unit = 16 if rng.random() < 0.8 else 8
+    widths = tuple(unit * int(rng.integers(1, 1 + 640 // unit)) for _ in range(S))
+    R = int(rng.choice([8, 16, 24, 32, 48, 64, 96, 128]))
+    slots = int(rng.integers(1, 65))
+    ranks = [int(rng.integers(0, R + 1)) if rng.random() < 0.8 else int(rng.choice([0, R]))
+             for _ in range(slots)]
+    return dict(T=T, in_f=in_f, out_slices=widths, R=R, slots=slots, ranks=ranks,
+                dead=float(rng.choice([0.0, 0.05, 0.3])), skew=float(rng.choice([0.0, 1.2, 2.0])))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(seed, fused):
+    case = _random_shape(seed)
+    log(f"random shape {seed} fused={fused}: T={case['T']} in={case['in_f']} "
+        f"out={case['out_slices']} R={case['R']} slots={case['slots']}")
+    wl = _custom(seed, **case)
+    tg = wl.targets[0]
+    _, h, y = GpuTarget(wl, tg).run(fused=fused)
+    h_ref, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y), y_ref, f"random {seed}")
+    r = np.array([min(max(int(wl.ranks[s]), 0), wl.R) if 0 <= s < wl.slots else 0
+                  for s in wl.token_slot])
+    same = r == 0   # rows of dead tokens and rank-0 slots are untouched, bit for bit
+    assert np.array_equal(f64(y)[same], O.decode(tg.y0, wl.dtype)[same])
+    if h is not None:   # the unfused shrink writes every read entry within the bound
+        read = ~unread_mask(wl, tg.num_slices)
+        assert_tol(f64(h)[read], h_ref[read], f"random {seed} h", atol=1e-3, rtol=1e-3)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("size", ["small", "full"])
 def test_router_fold(size, fused):
