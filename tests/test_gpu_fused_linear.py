@@ -182,3 +182,32 @@ def test_fused_column_linear_graph_equals_eager():
         t.cuda.synchronize()
         assert t.equal(addr.token_order, a_e.token_order)
         assert t.equal(y_graph, y_e), f"replay {rep}"
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("seed", range(8))
+def test_random_fused_column_linear(seed, fused):
+    """Seeded random shapes for the base projection with the delta in its
+    epilogue (and for our GEMM followed by lora_apply_linear): T, `in`, 1-3
+    slices of 256-multiples, rank, slots, ranks, dead tokens and skew drawn."""
+    rng = np.random.default_rng(4000 + seed)
+    T = int(rng.choice([int(rng.integers(1, 1024)), int(rng.integers(1024, 1800))]))
+    in_f = 8 * int(rng.integers(1, 97))
+    S = int(rng.integers(1, 4))
+    widths = tuple(256 * int(rng.integers(1, 4)) for _ in range(S))
+    R = int(rng.choice([8, 16, 32, 64, 128]))
+    slots = int(rng.integers(1, 40))
+    ranks = [int(rng.integers(0, R + 1)) for _ in range(slots)]
+    p = 1.0 / np.arange(1, slots + 1) ** float(rng.choice([0.0, 1.2]))
+    ts = rng.choice(slots, size=T, p=p / p.sum())
+    ts[rng.random(T) < 0.05] = -1
+    log(f"random fused linear {seed} fused={fused}: T={T} in={in_f} out={widths} R={R} "
+        f"slots={slots}")
+    wl = W.make_workload(name="random_fused_linear", dtype="bf16", T=T, in_features=in_f,
+                         out_slices=widths, R=R, slots=slots, ranks=ranks,
+                         scalings=rng.uniform(0.5, 2.0, size=slots), token_slot=ts, seed=seed,
+                         rng=rng)
+    tg = wl.targets[0]
+    w = W.base_weight(wl, tg)
+    y = _run(wl, tg, w, fused)
+    assert_tol(y, _reference(wl, tg, w), f"random fused linear {seed}")

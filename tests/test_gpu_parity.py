@@ -447,6 +447,59 @@ def test_random_shapes(seed, fused):
         assert_tol(f64(h)[read], h_ref[read], f"random {seed} h", atol=1e-3, rtol=1e-3)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_embedding(seed):
+    """Seeded random embedding batches: vocabulary, width, rank, slots, dead
+    tokens and bad ids drawn; gather_shrink's h bit-exact (zeros included),
+    y within the bound."""
+    rng = np.random.default_rng(2000 + seed)
+    T = int(rng.choice([int(rng.integers(1, 1024)), int(rng.integers(1024, 3000))]))
+    vocab = int(rng.integers(8, 20000))
+    out = int(rng.choice([8, 16])) * int(rng.integers(1, 64))
+    R = int(rng.choice([8, 16, 32, 64]))
+    slots = int(rng.integers(1, 17))
+    ranks = [int(rng.integers(0, R + 1)) for _ in range(slots)]
+    ts = rng.integers(0, slots, size=T)
+    ts[rng.random(T) < 0.05] = -1
+    ids = rng.integers(0, vocab, size=T).astype(np.int64)
+    bad = rng.random(T) < 0.05
+    ids[bad] = rng.choice([-1, vocab, vocab + 3, np.iinfo(np.int32).min], size=int(bad.sum()))
+    log(f"random embedding {seed}: T={T} vocab={vocab} out={out} R={R} slots={slots}")
+    wl = W.make_workload(name="random_embedding", dtype="bf16", T=T, in_features=vocab,
+                         out_slices=(out,), R=R, slots=slots, ranks=ranks,
+                         scalings=rng.uniform(0.5, 2.0, size=slots), token_slot=ts, seed=seed,
+                         rng=rng, ids=ids.astype(np.int32), a_std=1.0)
+    tg = wl.targets[0]
+    _, h, y = GpuTarget(wl, tg).run()
+    h_ref, y_ref = O.run_target(wl, tg)
+    assert np.array_equal(f64(h), h_ref)
+    assert_tol(f64(y), y_ref, f"random embedding {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_expert_addressing(seed):
+    """Seeded random expert-sorted batches: row count, experts, slots and
+    bounds drawn (rows before the first and after the last bound, empty
+    experts, bad slots); the device addressing equals the oracle's."""
+    t = torch()
+    rng = np.random.default_rng(3000 + seed)
+    rows = int(rng.integers(0, 4000))
+    E = int(rng.integers(1, 17))
+    slots = int(rng.integers(1, 65))
+    lo = int(rng.integers(0, max(1, rows // 8 + 1)))
+    hi = rows - int(rng.integers(0, max(1, rows // 8 + 1)))
+    hi = max(lo, hi)
+    offs = np.concatenate([[lo], np.sort(rng.integers(lo, hi + 1, size=E - 1)), [hi]]).astype(np.int32)
+    row_slot = rng.integers(-2, slots + 2, size=rows).astype(np.int32)
+    log(f"random expert addressing {seed}: rows={rows} E={E} slots={slots}")
+    addr = L.build_addressing_experts(t.from_numpy(row_slot).to("cuda:0"),
+                                      t.from_numpy(offs).to("cuda:0"), E, slots)
+    t.cuda.synchronize()
+    order, indptr = O.build_addressing_experts(row_slot, offs, E, slots)
+    assert np.array_equal(addr.token_order.cpu().numpy(), order)
+    assert np.array_equal(addr.slot_indptr.cpu().numpy(), indptr)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("size", ["small", "full"])
 def test_router_fold(size, fused):
