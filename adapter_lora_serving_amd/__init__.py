@@ -20,7 +20,8 @@ from typing import Optional, Sequence
 
 __all__ = [
     "Addressing", "LoraError", "lib", "lib_path", "build_addressing", "shrink",
-    "gather_shrink", "expand_", "expand_fused", "apply_linear_", "apply_", "Backend",
+    "gather_shrink", "expand_", "expand_fused", "apply_linear_", "apply_linear_from_slots_",
+    "from_slots_one_launch", "apply_", "Backend",
     "workspace_bytes", "STATUS", "column_linear", "fused_column_linear",
 ]
 
@@ -57,6 +58,12 @@ SIGNATURES = {
                                          _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "lora_apply_linear_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "lora_apply_linear_path": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P, _I32, _I32]),
+    "lora_apply_linear_from_slots": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32,
+                                                    _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                                    _SZ, _P]),
+    "lora_apply_linear_from_slots_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
+    "lora_apply_linear_from_slots_one_launch": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P, _I32,
+                                                               _I32, _I32]),
     "lora_apply_linear_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P,
                                                  _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "lora_noalloc_scratch_bytes": (_SZ, []),
@@ -305,6 +312,51 @@ def apply_linear_(x, y, a, b, addressing, ranks, scalings, out_slices: Sequence[
                                  _ptr(scalings), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(dev))
     _check(st, "lora_apply_linear")
+
+
+def apply_linear_from_slots_(x, y, a, b, token_slot, ranks, scalings, out_slices: Sequence[int],
+                             out: Optional[Addressing] = None, workspace=None) -> Addressing:
+    """Build the step's addressing from token_slot and apply a linear
+    target's delta into y in the same call (one kernel launch for a small
+    bf16 batch); returns the addressing for the step's later targets."""
+    import torch
+    token_slot = _i32(token_slot)
+    ranks = _i32(ranks)
+    dev = _dev(x, y, a, b, token_slot, ranks, scalings)
+    T, in_f = x.shape
+    slots, outw, R = b.shape
+    S = len(out_slices)
+    if (a.shape != (slots, S * R, in_f) or y.shape != (T, outw) or sum(out_slices) != outw
+            or token_slot.numel() != T):
+        raise LoraError("shape mismatch in apply_linear_from_slots_")
+    if out is None:
+        out = Addressing(torch.empty(T, dtype=torch.int32, device=dev),
+                         torch.empty(slots + 1, dtype=torch.int32, device=dev))
+    order, indptr = _addr(out)
+    _dev(x, order, indptr)
+    if (order.dtype != torch.int32 or indptr.dtype != torch.int32 or order.numel() != T
+            or indptr.numel() != slots + 1):
+        raise LoraError("the addressing to write must be int32 [T] and [slots + 1]")
+    need = int(lib().lora_apply_linear_from_slots_workspace_bytes(T, in_f, slots, S, R))
+    ws = _workspace(dev, need) if workspace is None else workspace
+    arr, S = _slices(out_slices)
+    st = lib().lora_apply_linear_from_slots(
+        _dtype_code(x), _ptr(x), _ptr(y), T, in_f, ctypes.cast(arr, _P), S, _ptr(a), _ptr(b),
+        slots, R, _ptr(token_slot), _ptr(order), _ptr(indptr), _ptr(ranks), _ptr(scalings),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "lora_apply_linear_from_slots")
+    return out
+
+
+def from_slots_one_launch(dtype_code: int, T: int, in_features: int, out_slices: Sequence[int],
+                          slots: int, R: int) -> bool:
+    """Whether apply_linear_from_slots_ is one kernel launch for these sizes."""
+    arr, S = _slices(out_slices)
+    r = int(lib().lora_apply_linear_from_slots_one_launch(dtype_code, T, in_features,
+                                                          ctypes.cast(arr, _P), S, slots, R))
+    if r < 0:
+        _check(-r, "lora_apply_linear_from_slots_one_launch")
+    return r == 1
 
 
 def apply_(x, y, a, b, addressing, ranks, scalings, out_slices: Sequence[int],

@@ -29,32 +29,6 @@ namespace {
 
 constexpr int kCache = 8;   // 64-token groups per wave kept in registers
 
-struct GroupMatch {
-  int key;      // -1 for a lane past the range
-  int rank;     // lanes below this one with the same key
-  int count;    // lanes with this key
-  bool leader;  // lowest lane with this key
-};
-
-// raw: the token's slot as stored (ignored when !valid)
-__device__ __forceinline__ GroupMatch match_raw(int raw, bool valid, int slots, int nbits) {
-  GroupMatch g;
-  int k = -1;
-  if (valid) k = (raw >= 0 && raw < slots) ? raw : slots;
-  uint64_t eq = __ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (k >> b) & 1;
-    const uint64_t bal = __ballot(valid && bit);
-    eq &= bit ? bal : ~bal;
-  }
-  const uint64_t below = eq & ((1ull << lane_id()) - 1ull);
-  g.key = k;
-  g.rank = __popcll(below);
-  g.count = __popcll(eq);
-  g.leader = valid && below == 0;
-  return g;
-}
-
 __device__ __forceinline__ GroupMatch match_group(const int32_t* __restrict__ token_slot, int t,
                                                   bool valid, int slots, int nbits) {
   return match_raw(valid ? token_slot[t] : -1, valid, slots, nbits);
@@ -154,48 +128,14 @@ __global__ __launch_bounds__(1024) void k_build_addressing(const int32_t* __rest
 }
 
 // Small batches over at most 63 slots: one wave sorts the whole batch (G
-// groups of 64 tokens, all slots loaded at once) with no workgroup barrier.
-// Per group, each lane's offset within its key is the key's count so far
-// (an LDS histogram of 64 entries) plus its rank among equal keys in the
-// group; lane k then holds key k for the scan that gives slot_indptr, and
-// the scatter adds the key's start.
+// groups of 64 tokens, all slots loaded at once) with no workgroup barrier
+// (addressing_one_wave).
 template <int G>
 __global__ __launch_bounds__(64) void k_build_addressing_wave(
     const int32_t* __restrict__ token_slot, int T, int slots, int32_t* __restrict__ token_order,
     int32_t* __restrict__ slot_indptr) {
   __shared__ int hist[kWave];
-  const int lane = lane_id();
-  const int nbits = 32 - __clz(slots);
-  int raw[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int t = g * kWave + lane;
-    raw[g] = t < T ? token_slot[t] : -1;
-  }
-  hist[lane] = 0;
-  __builtin_amdgcn_wave_barrier();
-  int key[G], off[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int t = g * kWave + lane;
-    const GroupMatch m = match_raw(raw[g], t < T, slots, nbits);
-    key[g] = m.key < 0 ? 0 : m.key;   // lanes past T: any valid index, never used
-    off[g] = hist[key[g]] + m.rank;
-    __builtin_amdgcn_wave_barrier();
-    if (m.leader) hist[m.key] += m.count;   // distinct keys: no two leaders collide
-    __builtin_amdgcn_wave_barrier();
-  }
-  const int c = lane <= slots ? hist[lane] : 0;
-  const int start = wave_inclusive_scan(c) - c;
-  if (lane <= slots) slot_indptr[lane] = start;
-  __builtin_amdgcn_wave_barrier();
-  hist[lane] = start;
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int t = g * kWave + lane;
-    if (t < T) token_order[hist[key[g]] + off[g]] = t;
-  }
+  addressing_one_wave<G>(token_slot, T, slots, token_order, slot_indptr, hist);
 }
 
 // Large batches with a workspace: two passes over blocks of 1024 tokens

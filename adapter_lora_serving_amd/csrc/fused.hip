@@ -29,6 +29,20 @@
 //   effectively fp32. Each lane then owns 4 consecutive columns of one token
 //   and rounds y once (nearest-even). B ranks at or past the rank are zeroed
 //   in registers.
+// One-launch form (lora_apply_linear_from_slots, at most 1024 tokens over at
+//   most 63 slots): the kernel takes each token's slot instead of the
+//   addressing, which the page builds once per step before the first
+//   target. A decode piece finds its slot's tokens itself (each wave loads
+//   the slot ids, one ballot per 64 tokens, and lane row m takes the m-th
+//   match: the same tokens in the same order as the stable grouping gives,
+//   so the result is bit-identical), a prefill item counts the slots in LDS
+//   to locate its item, and one workgroup writes the addressing for the
+//   step's later targets. A separate addressing kernel costs a whole launch
+//   (about 3.5 us of a 16 us step); finding the tokens per piece costs
+//   ~0.25 us of this kernel, because its vector loads queue behind the
+//   start-up flood of x and A loads where the addressing form's scalar
+//   reads of slot_indptr and token_order do not. (Reading the ids through
+//   scalar loads, 32 per wave, with one workgroup barrier, was slower.)
 #include "lora_common.h"
 #include "lora_kernels.h"
 
@@ -209,6 +223,8 @@ struct DecodeArgs {
   int KP;
   int spin_limit;
   int early;     // 1: read the partial entries once with the prefetch
+  bool tok_given;  // the lane's token id is tok_m (found from token_slot), not token_order's
+  int tok_m;
   uint32_t lg;   // log2 of the rank bucket RT: the low 3 bits of every tag
 };
 
@@ -247,6 +263,100 @@ __device__ __forceinline__ int lane_token_s(const int32_t* __restrict__ tokp, in
 #pragma unroll
   for (int k = 1; k < kMT; ++k) t = j == k ? ids[k] : t;
   return t;
+}
+
+// The tokens of slot s in ascending index, found from token_slot itself (the
+// one-launch form, T <= 2 * NW * 64): the ones at positions [first,
+// first + kMT) of the slot's list go to tok[0..kMT), `fill` past its end; the
+// return value is the slot's token count. This is the segment that the
+// addressing gives slot s (a stable grouping by slot), found with one
+// coalesced load and a ballot per 64 tokens instead of the two dependent
+// reads of slot_indptr and token_order. `cnt`: 2 * NW ints of LDS. Every
+// thread of the block calls it; the result is uniform.
+template <int NW>
+__device__ __forceinline__ int slot_tokens(const int32_t* __restrict__ token_slot, int T, int s,
+                                           int first, int fill, int* tok, int* cnt, int tid,
+                                           int lane, int w) {
+  constexpr int NT = NW * kWave;
+  const int t0 = tid;
+  const int t1 = tid + NT;
+  const bool m0 = t0 < T && token_slot[t0] == s;
+  const bool m1 = t1 < T && token_slot[t1] == s;
+  const uint64_t b0 = __ballot(m0);
+  const uint64_t b1 = __ballot(m1);
+  if (lane == 0) {
+    cnt[w] = __popcll(b0);        // tokens [64w, 64w + 64)
+    cnt[NW + w] = __popcll(b1);   // tokens [NT + 64w, NT + 64w + 64)
+  }
+  if (tid < kMT) tok[tid] = fill;
+  __syncthreads();
+  int before0 = 0, before1 = 0, total = 0;
+#pragma unroll
+  for (int c = 0; c < 2 * NW; ++c) {
+    const int v = cnt[c];
+    before0 += c < w ? v : 0;
+    before1 += c < NW + w ? v : 0;
+    total += v;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int p0 = before0 + __popcll(b0 & below) - first;
+  const int p1 = before1 + __popcll(b1 & below) - first;
+  if (m0 && p0 >= 0 && p0 < kMT) tok[p0] = t0;
+  if (m1 && p1 >= 0 && p1 < kMT) tok[p1] = t1;
+  __syncthreads();
+  return total;
+}
+
+// Position of the k-th set bit (k from 0, k < popcount) of a 64-bit mask,
+// by halving: six popcounts.
+__device__ __forceinline__ int nth_set_bit(uint64_t mask, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int width = 32; width >= 1; width >>= 1) {
+    const uint64_t low = mask & ((1ull << width) - 1ull);
+    const int c = __popcll(low);
+    if (k >= c) {
+      k -= c;
+      mask >>= width;
+      pos += width;
+    }
+  }
+  return pos;
+}
+
+// The decode pieces' form of slot_tokens, per wave and with no workgroup
+// barrier (each wave starts its loads as soon as it has its tokens, as with
+// token_order): the wave reads the T slot ids (T <= 1024, one 64-token group
+// per load), takes one ballot per group, and lane row m picks the m-th match
+// (0 when the slot has m tokens or fewer: such rows are not live). n receives
+// the slot's token count (uniform).
+__device__ __forceinline__ int wave_slot_token(const int32_t* __restrict__ token_slot, int T,
+                                               int s, int m, int& n) {
+  constexpr int kMaxGroups = 16;
+  const int lane = lane_id();
+  const int ng = (T + kWave - 1) / kWave;
+  int v[kMaxGroups];
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g) {
+    v[g] = -1;
+    if (g < ng) {
+      const int t = g * kWave + lane;
+      v[g] = t < T ? token_slot[t] : -1;
+    }
+  }
+  int count = 0;
+  int tok = 0;
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g) {
+    if (g < ng) {
+      const uint64_t mask = __ballot(v[g] == s);
+      const int c = __popcll(mask);
+      if (m >= count && m < count + c) tok = g * kWave + nth_set_bit(mask, m - count);
+      count += c;
+    }
+  }
+  n = count;
+  return tok;
 }
 
 // acc[nt] += x_block . A_rows(nt)^T for the first NT rank tiles, over K
@@ -455,7 +565,7 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
                                     __HIP_MEMORY_SCOPE_AGENT);
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = lane_token_s(d.tokp, d.T, seg0, m);
+  const int t = d.tok_given ? d.tok_m : lane_token_s(d.tokp, d.T, seg0, m);
   const bool live = m < n;
   const uint32_t rowA = (uint32_t)d.in * 2u;
   const int steps = (d.in + 31) / 32;
@@ -500,7 +610,7 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     ticket = __hip_atomic_fetch_add(cnts + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int m = lane & 15;
   const int kg = lane >> 4;
-  const int t = lane_token_s(d.tokp, d.T, seg0, m);
+  const int t = d.tok_given ? d.tok_m : lane_token_s(d.tokp, d.T, seg0, m);
   const bool live = m < n;
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
@@ -671,14 +781,22 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
 
 }  // namespace
 
-template <int RT, int NW>
+// FS (the one-launch form): the slot addressing is built in this launch.
+// Workgroup 0 runs the one-wave sort into order_out / indptr_out for later
+// calls on the same batch (workgroups 1-7 leave at once, so that the pieces
+// keep their XCD placement), and every piece finds its slot's tokens from
+// token_slot itself (slot_tokens); nothing in the launch reads the
+// addressing it writes. Needs T <= 2 * NW * 64 and slots + 1 <= 64.
+template <int RT, int NW, bool FS>
 __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     const void* __restrict__ x_, void* __restrict__ y_, int T, int in, SliceTable st,
     const void* __restrict__ a_, const void* __restrict__ b_, int slots, int R,
     const int32_t* __restrict__ token_order, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ ranks, const float* __restrict__ scalings, ChunkTable ct,
     int n_shrink, int n_expand, int nclass, int KP, uint64_t* __restrict__ part,
-    uint32_t* __restrict__ tickets, int spin_limit, int early) {
+    uint32_t* __restrict__ tickets, int spin_limit, int early,
+    const int32_t* __restrict__ token_slot, int32_t* __restrict__ order_out,
+    int32_t* __restrict__ indptr_out) {
   using L = Lds<RT, NW>;
   constexpr int RP = RT * 16;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -694,7 +812,20 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   const int S = st.n;
   const int SR = S * R;
   const int out = st.off[S];
-  const int bid = blockIdx.x;
+  int bid = blockIdx.x;
+  int* tcnt = (int*)red + kWave;   // slot_tokens' counts (red is free until a product)
+  if constexpr (FS) {
+    if (bid < 8) {
+      if (bid == 0 && w == 0) {
+        if (T <= 4 * kWave)
+          addressing_one_wave<4>(token_slot, T, slots, order_out, indptr_out, (int*)red);
+        else
+          addressing_one_wave<2 * NW>(token_slot, T, slots, order_out, indptr_out, (int*)red);
+      }
+      return;
+    }
+    bid -= 8;
+  }
 
   if (bid < n_shrink + n_expand) {
     // decode pieces; block bid = 8*k + xcd runs on XCD `xcd`, and every piece
@@ -721,8 +852,11 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     // the three loads are issued together; reading the rank first keeps the
     // compiler from waiting on the segment bounds before requesting it
     const int r_raw = __builtin_nontemporal_load(ranks + s);
-    int seg0, n;
-    segment_of(indptr, s, T, seg0, n);
+    int seg0 = 0, n, tm = 0;
+    if constexpr (FS)
+      tm = wave_slot_token(token_slot, T, s, lane & 15, n);
+    else
+      segment_of(indptr, s, T, seg0, n);
     const int r = clamp_rank(r_raw, R);
     if (r == 0 || n == 0 || n > kMT) return;
     if (nclass > 1 && cls != (2 * r > R ? 0 : 4 * r > R ? 1 : 2)) return;
@@ -738,6 +872,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     d.KP = KP;
     d.spin_limit = spin_limit;
     d.early = early;
+    d.tok_given = FS;
+    d.tok_m = tm;
     d.lg = RT == 1 ? 0u : RT == 2 ? 1u : RT == 4 ? 2u : RT == 8 ? 3u : 4u;
     const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * SR + (int64_t)i * R) * in * 2,
                                  (uint32_t)r * (uint32_t)in * 2u);
@@ -760,22 +896,39 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   }
 
   // prefill item: a block of 16 tokens of a long segment, every slice and column
+  int* hist = (int*)red;   // FS: per-slot token counts of the batch
+  if constexpr (FS) {
+    if (tid < kWave) hist[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += NW * kWave) {
+      const int v = token_slot[t];
+      if (v >= 0 && v < slots) atomicAdd(hist + v, 1);
+    }
+    __syncthreads();
+  }
   auto count = [&](int ss) -> int {
     int b0, nn;
-    segment_of(indptr, ss, T, b0, nn);
+    if constexpr (FS)
+      nn = hist[ss];
+    else
+      segment_of(indptr, ss, T, b0, nn);
     const int rr = clamp_rank(ranks[ss], R);
     return (nn > kMT && rr > 0) ? (nn + kMT - 1) / kMT : 0;
   };
   const SlotItem it = locate_item(bid - n_shrink - n_expand, slots, count, scratch);
   if (it.slot < 0) return;
   const int s = it.slot;
-  int seg0, n;
-  segment_of(indptr, s, T, seg0, n);
   const int r = clamp_rank(ranks[s], R);
   const int mb = it.local;
-  const int ntok = min(kMT, n - mb * kMT);
-  if (tid < kMT) tok[tid] = tid < ntok ? token_at(token_order, seg0 + mb * kMT + tid, T) : -1;
-  __syncthreads();
+  if constexpr (FS) {
+    slot_tokens<NW>(token_slot, T, s, mb * kMT, -1, tok, tcnt, tid, lane, w);
+  } else {
+    int seg0, n;
+    segment_of(indptr, s, T, seg0, n);
+    const int ntok = min(kMT, n - mb * kMT);
+    if (tid < kMT) tok[tid] = tid < ntok ? token_at(token_order, seg0 + mb * kMT + tid, T) : -1;
+    __syncthreads();
+  }
   const float scale = scalings[s];
   const char* ab = (const char*)a_ + (int64_t)s * SR * in * 2;
   const char* bb = (const char*)b_ + (int64_t)s * out * R * 2;
@@ -871,6 +1024,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_expand(
   d.KP = 1;
   d.spin_limit = 0;
   d.early = 0;
+  d.tok_given = false;
+  d.tok_m = 0;
   const rsrc_t b_r =
       make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
   expand_rows<RT, NW>(d, b_r, h, S * R, i * R, r, scalings[s], seg0, n, ct.c0[c], ct.c1[c], hhi,
@@ -973,6 +1128,11 @@ size_t fused_partial_bytes(int slots, int S, int R, int in) {
   return (size_t)slots * S * k_parts(in, 0, 1, 1) * kMT * RP * sizeof(uint64_t);
 }
 
+bool fused_from_slots_supported(int T, int slots) {
+  // slot_tokens covers 2 * 512 tokens; the one-wave sort 64 keys
+  return T <= 2 * kNW * kWave && slots + 1 <= kWave;
+}
+
 bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in) {
   if (dtype != kDtypeBF16) return false;
   // buffer offsets are 32-bit: every resource must stay below 2 GiB
@@ -991,8 +1151,11 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* token_slot, int32_t* order_out,
+                              int32_t* indptr_out) {
   if (T == 0) return hipSuccess;
+  const bool fs = token_slot != nullptr;
+  if (fs && !fused_from_slots_supported(T, slots)) return hipErrorInvalidValue;
   const ChunkTable ct = make_chunks(st, R, slots);
   const int KP = k_parts(in, st.off[st.n], slots, st.n);
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
@@ -1001,7 +1164,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int64_t n_shrink = nclass * slots8 * st.n * KP;
   const int64_t n_expand = nclass * slots8 * ct.n;
   const int64_t n_prefill = (T + kMT - 1) / kMT + slots;
-  const int64_t grid = n_shrink + n_expand + n_prefill;
+  const int64_t grid = n_shrink + n_expand + n_prefill + (fs ? 8 : 0);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   uint32_t* tickets = (uint32_t*)workspace;
   uint64_t* part = (uint64_t*)((char*)workspace + counter_bytes(slots, st.n));
@@ -1017,24 +1180,34 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int early = n_shrink + n_expand > 1024 ? 1 : 0;
   const int rt = rt_bucket(R);
   const size_t lds = lds_bytes(rt, kNW);
-#define LAUNCH(RTV)                                                                             \
+#define LAUNCH(RTV, FSV)                                                                        \
   do {                                                                                          \
     if (lds > 65536) {                                                                          \
-      hipError_t e = hipFuncSetAttribute((const void*)k_apply_fused<RTV, kNW>,                  \
+      hipError_t e = hipFuncSetAttribute((const void*)k_apply_fused<RTV, kNW, FSV>,             \
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
       if (e != hipSuccess) return e;                                                            \
     }                                                                                           \
-    hipLaunchKernelGGL((k_apply_fused<RTV, kNW>), dim3((unsigned)grid), dim3(kNW * 64), lds,    \
-                       stream, x, y, T, in, st, a, b, slots, R, token_order, indptr, ranks,     \
-                       scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part, tickets,    \
-                       spin_limit, early);                                                      \
+    hipLaunchKernelGGL((k_apply_fused<RTV, kNW, FSV>), dim3((unsigned)grid), dim3(kNW * 64),    \
+                       lds, stream, x, y, T, in, st, a, b, slots, R, token_order, indptr,       \
+                       ranks, scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part,     \
+                       tickets, spin_limit, early, token_slot, order_out, indptr_out);          \
   } while (0)
-  switch (rt) {
-    case 1: LAUNCH(1); break;
-    case 2: LAUNCH(2); break;
-    case 4: LAUNCH(4); break;
-    case 8: LAUNCH(8); break;
-    default: LAUNCH(16); break;
+  if (fs) {
+    switch (rt) {
+      case 1: LAUNCH(1, true); break;
+      case 2: LAUNCH(2, true); break;
+      case 4: LAUNCH(4, true); break;
+      case 8: LAUNCH(8, true); break;
+      default: LAUNCH(16, true); break;
+    }
+  } else {
+    switch (rt) {
+      case 1: LAUNCH(1, false); break;
+      case 2: LAUNCH(2, false); break;
+      case 4: LAUNCH(4, false); break;
+      case 8: LAUNCH(8, false); break;
+      default: LAUNCH(16, false); break;
+    }
   }
 #undef LAUNCH
   return hipGetLastError();

@@ -218,6 +218,49 @@ lora_status shrink_impl(int dtype, const void* x, int64_t T, int64_t in_features
   return hip_status(e);
 }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The kernels of lora_apply_linear once its arguments are checked.
+lora_status run_apply(int dtype, const void* x, void* y, int64_t T, int64_t in_features,
+                      const SliceTable& tab, int32_t num_slices, const void* a, const void* b,
+                      int32_t slots, int32_t R, const int32_t* token_order,
+                      const int32_t* slot_indptr, const int32_t* ranks, const float* scalings,
+                      void* workspace, hipStream_t s) {
+  float* h = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      lora::counter_bytes(slots, num_slices) +
+                                      partial_bytes(slots, num_slices, R, in_features));
+  const int path = apply_path(dtype, T, in_features, tab, R);
+  if (path != LORA_PATH_VALU) {
+    // The host picks the kernel family from the shapes only (fixed per
+    // captured graph): small batches run everything in the fused kernel
+    // (decode pieces for segments of at most 16 tokens, 16-token prefill
+    // items for longer ones); larger batches run every segment through the
+    // SGMV shrink and expand, which write and read their h in the
+    // workspace. There the few-token segments are pure weight streaming,
+    // which the SGMV tiles' shared, deeper loads serve better than the
+    // decode pieces.
+    hipError_t e;
+    if (path == LORA_PATH_FUSED) {
+      e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
+                                   token_order, slot_indptr, ranks, scalings, workspace, s);
+    } else {
+      const int kp = lora::sgmv_kparts((int)in_features);
+      float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);
+      e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                   token_order, slot_indptr, ranks, h, parts, kp, 0, s);
+      if (e == hipSuccess)
+        e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
+                                     ranks, scalings, 0, s);
+    }
+    return hip_status(e);
+  }
+  hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
+                                     token_order, slot_indptr, ranks, h, lora::kNoMaxSeg, s);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
+                                        slot_indptr, ranks, scalings, lora::kNoMaxSeg, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,40 +435,66 @@ lora_status lora_apply_linear(int dtype, const void* x, void* y, int64_t T, int6
   const size_t need = lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R);
   if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  return run_apply(dtype, x, y, T, in_features, tab, num_slices, a, b, slots, R, token_order,
+                   slot_indptr, ranks, scalings, workspace, (hipStream_t)stream);
+}
+
+int lora_apply_linear_from_slots_one_launch(int dtype, int64_t T, int64_t in_features,
+                                            const int64_t* out_slices, int32_t num_slices,
+                                            int32_t slots, int32_t R) {
+  const int path = lora_apply_linear_path(dtype, T, in_features, out_slices, num_slices, R);
+  if (path < 0) return path;
+  if (slots < 1 || slots > 8192) return -LORA_ERR_UNSUPPORTED;
+  return path == LORA_PATH_FUSED && T > 0 && lora::fused_from_slots_supported((int)T, slots);
+}
+
+size_t lora_apply_linear_from_slots_workspace_bytes(int64_t T, int64_t in_features,
+                                                    int32_t slots, int32_t num_slices,
+                                                    int32_t R) {
+  const size_t a = lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R);
+  if (a == 0) return 0;
+  // the apply's region, then the addressing's (the two-pass sort of a large batch)
+  return align256(a) + lora::addressing_workspace_bytes(T, slots);
+}
+
+lora_status lora_apply_linear_from_slots(int dtype, const void* x, void* y, int64_t T,
+                                         int64_t in_features, const int64_t* out_slices,
+                                         int32_t num_slices, const void* a, const void* b,
+                                         int32_t slots, int32_t R, const int32_t* token_slot,
+                                         int32_t* token_order, int32_t* slot_indptr,
+                                         const int32_t* ranks, const float* scalings,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  lora_status st = check_common(dtype, T, slots, R);
+  if (st != LORA_OK) return st;
+  SliceTable tab;
+  if ((st = make_slices(dtype, out_slices, num_slices, R, &tab)) != LORA_OK) return st;
+  if (in_features < 1 || in_features > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (!slot_indptr) return LORA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  float* h = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      lora::counter_bytes(slots, num_slices) +
-                                      partial_bytes(slots, num_slices, R, in_features));
-  const int path = apply_path(dtype, T, in_features, tab, R);
-  if (path != LORA_PATH_VALU) {
-    // The host picks the kernel family from the shapes only (fixed per
-    // captured graph): small batches run everything in the fused kernel
-    // (decode pieces for segments of at most 16 tokens, 16-token prefill
-    // items for longer ones); larger batches run every segment through the
-    // SGMV shrink and expand, which write and read their h in the
-    // workspace. There the few-token segments are pure weight streaming,
-    // which the SGMV tiles' shared, deeper loads serve better than the
-    // decode pieces.
-    hipError_t e;
-    if (path == LORA_PATH_FUSED) {
-      e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
-                                   token_order, slot_indptr, ranks, scalings, workspace, s);
-    } else {
-      const int kp = lora::sgmv_kparts((int)in_features);
-      float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);
-      e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                   token_order, slot_indptr, ranks, h, parts, kp, 0, s);
-      if (e == hipSuccess)
-        e = lora::launch_sgmv_expand(y, (int)T, tab, h, b, slots, R, token_order, slot_indptr,
-                                     ranks, scalings, 0, s);
-    }
-    return hip_status(e);
-  }
-  hipError_t e = lora::launch_shrink(dtype, x, (int)T, (int)in_features, a, slots, num_slices, R,
-                                     token_order, slot_indptr, ranks, h, lora::kNoMaxSeg, s);
+  if (T == 0)   // the addressing of an empty batch: slot_indptr all zeros
+    return hip_status(lora::launch_build_addressing(nullptr, 0, slots, nullptr, slot_indptr,
+                                                    nullptr, 0, s));
+  if (!x || !y || !a || !b || !scalings || !token_slot) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(a) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
+  if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  const size_t apply_need = align256(
+      lora_apply_linear_workspace_bytes(T, in_features, slots, num_slices, R));
+  const size_t need =
+      lora_apply_linear_from_slots_workspace_bytes(T, in_features, slots, num_slices, R);
+  if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  if (lora_apply_linear_from_slots_one_launch(dtype, T, in_features, out_slices, num_slices,
+                                              slots, R) == 1)
+    return hip_status(lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots,
+                                               R, nullptr, nullptr, ranks, scalings, workspace,
+                                               s, token_slot, token_order, slot_indptr));
+  const hipError_t e = lora::launch_build_addressing(
+      token_slot, (int)T, slots, token_order, slot_indptr,
+      static_cast<char*>(workspace) + apply_need, need - apply_need, s);
   if (e != hipSuccess) return LORA_ERR_HIP;
-  return hip_status(lora::launch_expand(dtype, y, (int)T, tab, h, b, slots, R, token_order,
-                                        slot_indptr, ranks, scalings, lora::kNoMaxSeg, s));
+  return run_apply(dtype, x, y, T, in_features, tab, num_slices, a, b, slots, R, token_order,
+                   slot_indptr, ranks, scalings, workspace, s);
 }
 
 }  // extern "C"

@@ -337,4 +337,87 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+
+// ---------------------------------------------------------------------------
+// Slot addressing pieces shared by the addressing kernels and the fused
+// kernel's one-launch form (which builds the addressing in one workgroup of
+// the same launch).
+
+// Lanes of a wave holding the same key: dead tokens (slot outside
+// [0, slots)) take key `slots`, after every live slot.
+struct GroupMatch {
+  int key;      // -1 for a lane past the range
+  int rank;     // lanes below this one with the same key
+  int count;    // lanes with this key
+  bool leader;  // lowest lane with this key
+};
+
+// raw: the token's slot as stored (ignored when !valid). One ballot per key
+// bit (nbits = bits of `slots`), independent of how many distinct keys the
+// wave holds.
+__device__ __forceinline__ GroupMatch match_raw(int raw, bool valid, int slots, int nbits) {
+  GroupMatch g;
+  int k = -1;
+  if (valid) k = (raw >= 0 && raw < slots) ? raw : slots;
+  uint64_t eq = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (k >> b) & 1;
+    const uint64_t bal = __ballot(valid && bit);
+    eq &= bit ? bal : ~bal;
+  }
+  const uint64_t below = eq & ((1ull << lane_id()) - 1ull);
+  g.key = k;
+  g.rank = __popcll(below);
+  g.count = __popcll(eq);
+  g.leader = valid && below == 0;
+  return g;
+}
+
+// Stable counting sort of tokens [0, T) by slot in one wave, for T <= G * 64
+// and slots + 1 <= 64 keys, with no workgroup barrier: token_order lists each
+// slot's tokens in ascending index (dead tokens last), slot_indptr[s] is
+// where slot s begins (slots + 1 entries). Per group of 64 tokens, a lane's
+// offset within its key is the key's count so far (an LDS histogram, `hist`:
+// 64 ints) plus its rank among equal keys in the group; lane k then holds
+// key k for the scan that gives slot_indptr, and the scatter adds the key's
+// start.
+template <int G>
+__device__ __forceinline__ void addressing_one_wave(const int32_t* __restrict__ token_slot, int T,
+                                                    int slots, int32_t* __restrict__ token_order,
+                                                    int32_t* __restrict__ slot_indptr,
+                                                    int* hist) {
+  const int lane = lane_id();
+  const int nbits = 32 - __clz(slots);
+  int raw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    raw[g] = t < T ? token_slot[t] : -1;
+  }
+  hist[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  int key[G], off[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    const GroupMatch m = match_raw(raw[g], t < T, slots, nbits);
+    key[g] = m.key < 0 ? 0 : m.key;   // lanes past T: any valid index, never used
+    off[g] = hist[key[g]] + m.rank;
+    __builtin_amdgcn_wave_barrier();
+    if (m.leader) hist[m.key] += m.count;   // distinct keys: no two leaders collide
+    __builtin_amdgcn_wave_barrier();
+  }
+  const int c = lane <= slots ? hist[lane] : 0;
+  const int start = wave_inclusive_scan(c) - c;
+  if (lane <= slots) slot_indptr[lane] = start;
+  __builtin_amdgcn_wave_barrier();
+  hist[lane] = start;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    if (t < T) token_order[hist[key[g]] + off[g]] = t;
+  }
+}
+
 }  // namespace lora

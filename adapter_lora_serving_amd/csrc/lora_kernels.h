@@ -103,11 +103,17 @@ hipError_t launch_decode_expand(void* y, int T, const SliceTable& st, const floa
 
 // The fused kernel for a small batch: decode pieces for segments of at most
 // 16 tokens, 16-token prefill items over every column for longer ones.
+// With token_slot (the one-launch form, where fused_from_slots_supported
+// holds), the kernel builds the addressing itself: order_out / indptr_out
+// receive what launch_build_addressing writes, and token_order / indptr are
+// not read.
 hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const SliceTable& st,
                               const void* a, const void* b, int slots, int R,
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
-                              hipStream_t stream);
+                              hipStream_t stream, const int32_t* token_slot = nullptr,
+                              int32_t* order_out = nullptr, int32_t* indptr_out = nullptr);
+bool fused_from_slots_supported(int T, int slots);
 
 // The base projection y = x @ W^T of a fused linear layer (W [out, in], the
 // shards stacked along out) with the LoRA delta of h (fp32 [T, S*R], from

@@ -3,7 +3,10 @@
 
 A step is one pass of the whole hot path over one batch: the device-side
 addressing build, then the fused shrink + expand (lora_apply_linear) of a
-linear target, or gather_shrink + expand of an embedding target. The default
+linear target, or gather_shrink + expand of an embedding target. Where the
+library does both in one launch (lora_apply_linear_from_slots: a bf16 batch
+of at most 1024 tokens over at most 63 slots) the step is that one call,
+which also writes the addressing for the step's later targets. The default
 workload is the decode BGMV batch: T=256 tokens, one per request, in=4096,
 fused q/k/v out_slices (4096, 1024, 1024), 32 adapter slots with ranks in
 {8, 16} (R=16), scaling 2, bf16, seeded synthetic data. `--config 3|4|5`
@@ -14,9 +17,11 @@ Timing: the inputs of `--sets` independent buffer sets are resident in HBM
 step i uses set i mod sets. The K timed steps are recorded once in a hipGraph
 (through torch.cuda.CUDAGraph) and replayed once between two synchronisations,
 so host launch overhead is not measured. The dominant kernel's average launch
-duration comes from HIP events around a second graph that launches only the
-apply (lora_apply_linear, or gather_shrink + expand) K times on the same
-stream.
+duration: the step's own where it is one launch, else HIP events around a
+second graph that launches only the apply (lora_apply_linear, or
+gather_shrink + expand) K times on the same stream. The addressing alone,
+the apply alone and (for a one-launch step) the two-launch step are timed
+the same way and reported beside it.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -402,10 +407,28 @@ def main():
             L.apply_linear_(s["x"], s["y"], s["a"], s["b"], s["addr"], ranks, scal,
                             tg.out_slices, workspace=ws)
 
-    def step(i):
+    # The first linear target of a small batch builds the step's addressing
+    # in its own launch (lora_apply_linear_from_slots): the step is then one
+    # kernel, which also writes token_order and slot_indptr for the step's
+    # later targets. Elsewhere the addressing kernel runs first.
+    one_launch = (not tg.embedding and ex is None and L.from_slots_one_launch(
+        1 if wl.dtype == "bf16" else 0, wl.T, tg.in_features, tg.out_slices, wl.slots, wl.R))
+    if one_launch:
+        need_fs = int(L.lib().lora_apply_linear_from_slots_workspace_bytes(
+            wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R))
+        ws_fs = torch.zeros(max(need_fs, 256), dtype=torch.uint8, device=dev)
+
+    def step_two_launch(i):
         s = sets[i % n_sets]
         addressing(s, out=s["addr"])
         apply_only(i)
+
+    def step(i):
+        if not one_launch:
+            return step_two_launch(i)
+        s = sets[i % n_sets]
+        L.apply_linear_from_slots_(s["x"], s["y"], s["a"], s["b"], s["ts"], ranks, scal,
+                                   tg.out_slices, out=s["addr"], workspace=ws_fs)
 
     def addr_only(i):
         s = sets[i % n_sets]
@@ -430,6 +453,7 @@ def main():
     g_step = capture(step, K)
     g_apply = capture(apply_only, K)
     g_addr = capture(addr_only, K)
+    g_two = capture(step_two_launch, K) if one_launch else None
 
     def timed(g):
         g.replay()                     # untimed replay: graph upload, caches of the code
@@ -447,6 +471,15 @@ def main():
     ms_step = ms_total / K
     ms_apply = timed(g_apply) / K
     ms_addr = timed(g_addr) / K
+    ms_two = timed(g_two) / K if one_launch else None
+    # the dominant kernel: the step's one launch (it also reads token_slot,
+    # counted in the metadata term, and writes the addressing), else the apply
+    if one_launch:
+        ms_kernel = ms_step
+        kernel_bytes = alg_bytes + 4 * wl.T + 4 * (wl.slots + 1)
+    else:
+        ms_kernel = ms_apply
+        kernel_bytes = alg_bytes
 
     # sanity denominator: a plain device copy of 1 GiB
     src = torch.empty(2 ** 28, dtype=torch.float32, device=dev)
@@ -474,11 +507,14 @@ def main():
     ms_copy = timed(g_copy) / K
     del g_copy, pairs
 
-    achieved = alg_bytes / (ms_apply * 1e-3) / 1e9
+    achieved = kernel_bytes / (ms_kernel * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_step * 1e-3)
-    eprint(f"step {ms_step * 1e3:.2f} us (addressing {ms_addr * 1e3:.2f} us, apply "
-           f"{ms_apply * 1e3:.2f} us/launch = {achieved:.0f} GB/s algorithmic); device copy "
-           f"{copy_gbs:.0f} GB/s; a copy of the same bytes {ms_copy * 1e3:.2f} us")
+    eprint(f"step {ms_step * 1e3:.2f} us ({'one launch' if one_launch else 'two launches'}; "
+           f"{achieved:.0f} GB/s algorithmic); addressing alone {ms_addr * 1e3:.2f} us, apply "
+           f"alone {ms_apply * 1e3:.2f} us"
+           + (f", addressing then apply {ms_two * 1e3:.2f} us" if one_launch else "")
+           + f"; device copy {copy_gbs:.0f} GB/s; a copy of the same bytes "
+           f"{ms_copy * 1e3:.2f} us")
 
     result = {
         "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill)",
@@ -498,18 +534,21 @@ def main():
                    "slots": wl.slots, "buffer_sets": n_sets},
         "roofline": {
             "bound": "hbm",
-            "kernel": "lora_gather_shrink + lora_expand" if tg.embedding else "lora_apply_linear",
+            "kernel": ("lora_gather_shrink + lora_expand" if tg.embedding else
+                       "lora_apply_linear_from_slots" if one_launch else "lora_apply_linear"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(wl.name if len(wl.targets) == 1
                                         else f"{wl.name}_{tg.name}"),
-            "algorithmic_bytes_per_launch": int(alg_bytes),
-            "avg_launch_us": round(ms_apply * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(kernel_bytes),
+            "avg_launch_us": round(ms_kernel * 1e3, 3),
         },
-        "mfma_util": round(alg_flops / (ms_apply * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 5),
+        "mfma_util": round(alg_flops / (ms_kernel * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 5),
         "addressing_us": round(ms_addr * 1e3, 3),
+        "apply_only_us": round(ms_apply * 1e3, 3),
+        "addressing_then_apply_us": round((ms_two if one_launch else ms_step) * 1e3, 3),
         "device_copy_gbs": round(copy_gbs, 1),
         "device_copy_same_bytes_us": round(ms_copy * 1e3, 3),
     }

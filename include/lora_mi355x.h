@@ -260,6 +260,51 @@ int lora_apply_linear_path(int dtype, int64_t T, int64_t in_features, const int6
                            int32_t num_slices, int32_t R);
 
 /*
+ * lora_apply_linear_from_slots: lora_build_addressing followed by
+ * lora_apply_linear, for the first linear target of a step.
+ *
+ * Source: lora.backend, module overview (the addressing is made once per
+ * step from each token's slot, and every target's shrink and expand then
+ * use it) and LoraBackend.apply_linear_. Arguments as lora_apply_linear,
+ * except that token_slot (device, int32 [T]: each token's slot; a value
+ * outside [0, slots) means no adapter) replaces the addressing, which this
+ * call writes instead: token_order (device, int32 [T]) and slot_indptr
+ * (device, int32 [slots + 1]) receive exactly what lora_build_addressing
+ * writes, for the step's later targets, and y receives exactly (bit for bit)
+ * what lora_apply_linear gives with that addressing.
+ * Where lora_apply_linear_from_slots_one_launch(...) is 1 (the fused path of
+ * a small bf16 batch, T <= 1024, slots <= 63) it is one kernel launch: each
+ * piece finds its slot's tokens from token_slot itself and one workgroup
+ * writes the addressing, which nothing in that launch reads. Elsewhere the
+ * addressing kernel runs first, then lora_apply_linear's kernels.
+ * workspace: at least lora_apply_linear_from_slots_workspace_bytes(...)
+ * bytes, under lora_apply_linear's rules (256-byte aligned, zero-filled
+ * before its first use, one per stream; shared with lora_apply_linear calls
+ * on the same stream). T == 0 writes slot_indptr (all zeros) only.
+ */
+lora_status lora_apply_linear_from_slots(int dtype, const void* x, void* y, int64_t T,
+                                         int64_t in_features, const int64_t* out_slices,
+                                         int32_t num_slices, const void* a, const void* b,
+                                         int32_t slots, int32_t R, const int32_t* token_slot,
+                                         int32_t* token_order, int32_t* slot_indptr,
+                                         const int32_t* ranks, const float* scalings,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lora_apply_linear_from_slots needs (0 on bad input). */
+size_t lora_apply_linear_from_slots_workspace_bytes(int64_t T, int64_t in_features,
+                                                    int32_t slots, int32_t num_slices,
+                                                    int32_t R);
+
+/*
+ * lora_apply_linear_from_slots_one_launch: 1 when lora_apply_linear_from_slots
+ * runs as one kernel launch for these sizes, 0 when the addressing kernel runs
+ * first, a negated lora_status for bad arguments (host-only query).
+ */
+int lora_apply_linear_from_slots_one_launch(int dtype, int64_t T, int64_t in_features,
+                                            const int64_t* out_slices, int32_t num_slices,
+                                            int32_t slots, int32_t R);
+
+/*
  * lora_column_linear: the base projection of a fused column-parallel linear
  * layer, y = x @ W^T, on the library's bf16 MFMA GEMM.
  *

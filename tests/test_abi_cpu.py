@@ -224,6 +224,54 @@ def test_apply_linear_path_predicate(lib):
     assert f(1, 256, 4096, _slices(12), 1, 16) == -ALIGN
 
 
+def test_from_slots_validation_and_path(lib):
+    """The one-launch form (addressing built in the same call) refuses bad
+    host arguments before any launch, sizes its workspace as the apply's
+    plus the addressing's, and is one launch exactly for the fused path of
+    a batch of at most 1024 tokens over at most 63 slots."""
+    qkv = _slices(4096, 1024, 1024)
+    one = lib.lora_apply_linear_from_slots_one_launch
+    assert one(1, 256, 4096, qkv, 3, 32, 16) == 1
+    assert one(1, 1, 4096, qkv, 3, 63, 16) == 1
+    assert one(1, 1023, 4096, qkv, 3, 32, 16) == 1
+    assert one(1, 256, 4096, qkv, 3, 64, 16) == 0                 # the sort needs 64 keys or fewer
+    assert one(1, 1024, 4096, qkv, 3, 32, 16) == 0                # segment path
+    assert one(0, 256, 4096, qkv, 3, 32, 16) == 0                 # fp32: vector kernels
+    assert one(1, 0, 4096, qkv, 3, 32, 16) == 0
+    assert one(7, 256, 4096, qkv, 3, 32, 16) == -UNSUPPORTED
+    assert one(1, 256, 4096, qkv, 3, 0, 16) == -UNSUPPORTED
+
+    wsb = lib.lora_apply_linear_from_slots_workspace_bytes
+    apply_need = lib.lora_apply_linear_workspace_bytes(256, 4096, 32, 3, 16)
+    assert wsb(256, 4096, 32, 3, 16) == (apply_need + 255) // 256 * 256
+    big = lib.lora_apply_linear_workspace_bytes(8192, 4096, 32, 3, 16)
+    assert wsb(8192, 4096, 32, 3, 16) == (big + 255) // 256 * 256 + 8 * 33 * 4   # two-pass sort
+    assert wsb(-1, 4096, 32, 3, 16) == 0
+    need = wsb(256, 4096, 32, 3, 16)
+
+    f = lib.lora_apply_linear_from_slots
+
+    def call(dtype=1, x=A16, T=256, inf=4096, R=16, slot=A16, order=A16, indptr=A16, ranks=A16,
+             ws=A16, nbytes=need):
+        return f(dtype, x, A16, T, inf, qkv, 3, A16, A16, 32, R, slot, order, indptr, ranks,
+                 A16, ws, nbytes, None)
+
+    assert call(dtype=5) == UNSUPPORTED
+    assert call(R=0) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(inf=0) == INVALID
+    assert call(indptr=None) == INVALID
+    assert call(slot=None) == INVALID
+    assert call(order=None) == INVALID
+    assert call(ranks=None) == INVALID
+    assert call(x=None) == INVALID
+    assert call(x=MIS) == ALIGN
+    assert call(inf=4100) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(ws=A16 + 16) == ALIGN
+
+
 def test_noalloc_limits_checked_on_host(lib):
     """lora_apply_linear_noalloc refuses sizes beyond its static scratch array
     (LORA_ERR_SCRATCH_LIMIT) and bad scalars (as lora_apply_linear does)
