@@ -48,6 +48,10 @@
 
 #include <stdlib.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace lora {
 
 namespace {
@@ -1050,6 +1054,47 @@ int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
+const void* fused_kernel(int rt, bool fs) {
+  if (fs) {
+    switch (rt) {
+      case 1: return (const void*)k_apply_fused<1, kNW, true>;
+      case 2: return (const void*)k_apply_fused<2, kNW, true>;
+      case 4: return (const void*)k_apply_fused<4, kNW, true>;
+      case 8: return (const void*)k_apply_fused<8, kNW, true>;
+      default: return (const void*)k_apply_fused<16, kNW, true>;
+    }
+  }
+  switch (rt) {
+    case 1: return (const void*)k_apply_fused<1, kNW, false>;
+    case 2: return (const void*)k_apply_fused<2, kNW, false>;
+    case 4: return (const void*)k_apply_fused<4, kNW, false>;
+    case 8: return (const void*)k_apply_fused<8, kNW, false>;
+    default: return (const void*)k_apply_fused<16, kNW, false>;
+  }
+}
+
+// Workgroups of a kernel instance that the current device holds at once
+// (occupancy per CU x CUs), cached per instance and device; 0 if the
+// runtime cannot say.
+int64_t resident_blocks(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(fn, dev);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess)
+    per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int64_t r = (int64_t)per_cu * cus;
+  cache[key] = r;
+  return r;
+}
+
 int decode_chunk_cols(int R, int out, int slots) {
   // columns per decode expand piece: 1024 up to rank 32, else 2048; twice
   // that when a batch of many slots would otherwise make more than 4096
@@ -1157,7 +1202,28 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const bool fs = token_slot != nullptr;
   if (fs && !fused_from_slots_supported(T, slots)) return hipErrorInvalidValue;
   const ChunkTable ct = make_chunks(st, R, slots);
-  const int KP = k_parts(in, st.off[st.n], slots, st.n);
+  const int rt = rt_bucket(R);
+  const size_t lds = lds_bytes(rt, kNW);
+  const void* fn = fused_kernel(rt, fs);
+  if (lds > 65536) {
+    hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  int KP = k_parts(in, st.off[st.n], slots, st.n);
+  if (env_int("LORA_KPARTS", 0) <= 0) {
+    // More K parts while every live piece (one per slot, slice and part, and
+    // one per slot and column chunk) still fits on the chip at once, and each
+    // part stays at least 1024 deep: more shrink pieces put more loads in
+    // flight (the 32-slot qkv decode, 2 -> 3 parts: 480 pieces, 12.46 ->
+    // 12.29 us per step; 4 parts make 576, more than the 512 the chip holds,
+    // and take 16.9 us)
+    const int64_t resident = resident_blocks(fn, kNW * kWave, lds);
+    const int64_t live_expand = (int64_t)slots * ct.n;
+    while (KP < 8 && in / (KP + 1) >= 1024 &&
+           (int64_t)slots * st.n * (KP + 1) + live_expand <= resident)
+      ++KP;
+  }
   const int64_t slots8 = 8 * (int64_t)((slots + 7) / 8);
   // rank classes (largest first) where ranks differ enough to matter
   const int nclass = rt_bucket(R) >= 4 ? 3 : 1;
@@ -1178,15 +1244,8 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   // 38.8 -> 37.4 us (down); on grids that run at once (the 32-slot decode,
   // a router's logits) the reads cost ~0.3 us
   const int early = n_shrink + n_expand > 1024 ? 1 : 0;
-  const int rt = rt_bucket(R);
-  const size_t lds = lds_bytes(rt, kNW);
 #define LAUNCH(RTV, FSV)                                                                        \
   do {                                                                                          \
-    if (lds > 65536) {                                                                          \
-      hipError_t e = hipFuncSetAttribute((const void*)k_apply_fused<RTV, kNW, FSV>,             \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
-      if (e != hipSuccess) return e;                                                            \
-    }                                                                                           \
     hipLaunchKernelGGL((k_apply_fused<RTV, kNW, FSV>), dim3((unsigned)grid), dim3(kNW * 64),    \
                        lds, stream, x, y, T, in, st, a, b, slots, R, token_order, indptr,       \
                        ranks, scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part,     \
