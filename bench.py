@@ -327,7 +327,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
