@@ -542,14 +542,19 @@ def test_tp8_prefill_share(name):
     assert_tol(f64(y), y_ref, f"tp8 prefill share {name}")
 
 
-@pytest.mark.parametrize("rows,E,slots", [(300, 8, 16), (2000, 8, 32), (5000, 64, 64)])
+@pytest.mark.parametrize("rows,E,slots", [
+    (300, 8, 16), (2000, 8, 32), (5000, 64, 64),
+    # one row, one expert, 63 and 1023 virtual slots, 1024 and 1025 rows
+    (1, 1, 1), (64, 1, 63), (65, 3, 21), (512, 8, 32), (1024, 31, 33), (1024, 1, 1023),
+    (1025, 31, 33), (1024, 32, 32), (700, 128, 8)])
 def test_expert_addressing_bit_exact(rows, E, slots):
     """The device addressing of an expert-sorted batch equals the oracle's,
     bit for bit (dead rows: bad slots and rows outside the expert bounds)."""
     t = torch()
-    rng = np.random.default_rng(rows)
+    rng = np.random.default_rng(rows * 7 + E)
     cuts = np.sort(rng.integers(0, rows + 1, size=E - 1))
-    offs = np.concatenate([[3], cuts.clip(3, rows - 2), [rows - 2]]).astype(np.int32)
+    lo, hi = min(3, rows // 4), max(rows - 2, rows - rows // 4)
+    offs = np.concatenate([[lo], cuts.clip(lo, hi), [hi]]).astype(np.int32)
     row_slot = rng.integers(-1, slots + 1, size=rows).astype(np.int32)
     addr = L.build_addressing_experts(t.from_numpy(row_slot).to("cuda:0"),
                                       t.from_numpy(offs).to("cuda:0"), E, slots)
