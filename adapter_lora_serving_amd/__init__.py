@@ -21,7 +21,8 @@ from typing import Optional, Sequence
 __all__ = [
     "Addressing", "LoraError", "lib", "lib_path", "build_addressing", "shrink",
     "gather_shrink", "expand_", "expand_fused", "apply_linear_", "apply_linear_from_slots_",
-    "from_slots_one_launch", "apply_", "Backend",
+    "from_slots_one_launch", "apply_linear_from_experts_", "from_experts_one_launch", "apply_",
+    "Backend",
     "workspace_bytes", "STATUS", "column_linear", "fused_column_linear",
 ]
 
@@ -64,6 +65,13 @@ SIGNATURES = {
     "lora_apply_linear_from_slots_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32]),
     "lora_apply_linear_from_slots_one_launch": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P, _I32,
                                                                _I32, _I32]),
+    "lora_apply_linear_from_experts": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32,
+                                                      _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                                      _P, _P, _P, _SZ, _P]),
+    "lora_apply_linear_from_experts_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I32,
+                                                             _I32]),
+    "lora_apply_linear_from_experts_one_launch": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _P,
+                                                                 _I32, _I32, _I32, _I32]),
     "lora_apply_linear_noalloc": (ctypes.c_int, [ctypes.c_int, _P, _P, _I64, _I64, _P, _I32, _P,
                                                  _P, _I32, _I32, _P, _P, _P, _P, _P]),
     "lora_noalloc_scratch_bytes": (_SZ, []),
@@ -346,6 +354,59 @@ def apply_linear_from_slots_(x, y, a, b, token_slot, ranks, scalings, out_slices
         _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(st, "lora_apply_linear_from_slots")
     return out
+
+
+def apply_linear_from_experts_(x, y, a, b, row_slot, expert_offsets, num_experts: int,
+                               slots: int, ranks, scalings, out_slices: Sequence[int],
+                               out: Optional[Addressing] = None, workspace=None) -> Addressing:
+    """Build the expert addressing of an expert-sorted batch and apply a
+    routed-expert target's delta into y in the same call (one kernel launch
+    for a small bf16 batch); a, b, ranks and scalings are per pool entry
+    expert * slots + slot. Returns the addressing for the step's later
+    targets."""
+    import torch
+    row_slot = _i32(row_slot)
+    expert_offsets = _i32(expert_offsets)
+    ranks = _i32(ranks)
+    dev = _dev(x, y, a, b, row_slot, expert_offsets, ranks, scalings)
+    rows, in_f = x.shape
+    K, outw, R = b.shape
+    S = len(out_slices)
+    if (K != num_experts * slots or a.shape != (K, S * R, in_f) or y.shape != (rows, outw)
+            or sum(out_slices) != outw or row_slot.numel() != rows
+            or expert_offsets.numel() != num_experts + 1):
+        raise LoraError("shape mismatch in apply_linear_from_experts_")
+    if out is None:
+        out = Addressing(torch.empty(rows, dtype=torch.int32, device=dev),
+                         torch.empty(K + 1, dtype=torch.int32, device=dev))
+    order, indptr = _addr(out)
+    _dev(x, order, indptr)
+    if (order.dtype != torch.int32 or indptr.dtype != torch.int32 or order.numel() != rows
+            or indptr.numel() != K + 1):
+        raise LoraError("the addressing to write must be int32 [rows] and [experts * slots + 1]")
+    need = int(lib().lora_apply_linear_from_experts_workspace_bytes(rows, in_f, num_experts,
+                                                                     slots, S, R))
+    ws = _workspace(dev, need) if workspace is None else workspace
+    arr, S = _slices(out_slices)
+    st = lib().lora_apply_linear_from_experts(
+        _dtype_code(x), _ptr(x), _ptr(y), rows, in_f, ctypes.cast(arr, _P), S, _ptr(a), _ptr(b),
+        num_experts, slots, R, _ptr(row_slot), _ptr(expert_offsets), _ptr(order), _ptr(indptr),
+        _ptr(ranks), _ptr(scalings), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "lora_apply_linear_from_experts")
+    return out
+
+
+def from_experts_one_launch(dtype_code: int, rows: int, in_features: int,
+                            out_slices: Sequence[int], num_experts: int, slots: int,
+                            R: int) -> bool:
+    """Whether apply_linear_from_experts_ is one kernel launch for these sizes."""
+    arr, S = _slices(out_slices)
+    r = int(lib().lora_apply_linear_from_experts_one_launch(dtype_code, rows, in_features,
+                                                            ctypes.cast(arr, _P), S, num_experts,
+                                                            slots, R))
+    if r < 0:
+        _check(-r, "lora_apply_linear_from_experts_one_launch")
+    return r == 1
 
 
 def from_slots_one_launch(dtype_code: int, T: int, in_features: int, out_slices: Sequence[int],

@@ -227,27 +227,14 @@ size_t addressing_lds_bytes(int nw, int slots) {
   return (size_t)((nw + 1) * (slots + 1) + 20) * sizeof(int);
 }
 
-// Composite key of each row of an expert-sorted batch: expert e of row r is
-// the e with offs[e] <= r < offs[e + 1]; key = e * slots + row_slot[r], or
-// -1 (dead) for a slot outside [0, slots) or a row outside [offs[0],
-// offs[E]). A malformed offs gives wrong keys but no access out of bounds.
+// Composite key of each row of an expert-sorted batch (expert_key).
 __global__ __launch_bounds__(256) void k_expert_keys(const int32_t* __restrict__ row_slot,
                                                      const int32_t* __restrict__ offs, int E,
                                                      int rows, int slots,
                                                      int32_t* __restrict__ keys) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
-  int key = -1;
-  if (r >= offs[0] && r < offs[E]) {
-    int lo = 0, hi = E;   // invariant: offs[lo] <= r < offs[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (offs[mid] <= r) lo = mid; else hi = mid;
-    }
-    const int s = row_slot[r];
-    if (s >= 0 && s < slots) key = lo * slots + s;
-  }
-  keys[r] = key;
+  keys[r] = expert_key(r, row_slot[r], offs, E, slots);
 }
 
 size_t addressing_workspace_bytes(int64_t T, int slots) {

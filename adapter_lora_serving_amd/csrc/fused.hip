@@ -269,23 +269,23 @@ __device__ __forceinline__ int lane_token_s(const int32_t* __restrict__ tokp, in
   return t;
 }
 
-// The tokens of slot s in ascending index, found from token_slot itself (the
-// one-launch form, T <= 2 * NW * 64): the ones at positions [first,
-// first + kMT) of the slot's list go to tok[0..kMT), `fill` past its end; the
-// return value is the slot's token count. This is the segment that the
+// The tokens t in [lo, hi) with ids[t] == s, in ascending index, found
+// from the ids themselves (the one-launch forms, hi - lo <= 2 * NW * 64):
+// the ones at positions [first, first + kMT) of that list go to
+// tok[0..kMT), `fill` past its end; the return value is their count. This is the segment that the
 // addressing gives slot s (a stable grouping by slot), found with one
 // coalesced load and a ballot per 64 tokens instead of the two dependent
 // reads of slot_indptr and token_order. `cnt`: 2 * NW ints of LDS. Every
 // thread of the block calls it; the result is uniform.
 template <int NW>
-__device__ __forceinline__ int slot_tokens(const int32_t* __restrict__ token_slot, int T, int s,
-                                           int first, int fill, int* tok, int* cnt, int tid,
+__device__ __forceinline__ int slot_tokens(const int32_t* __restrict__ ids, int lo, int hi,
+                                           int s, int first, int fill, int* tok, int* cnt, int tid,
                                            int lane, int w) {
   constexpr int NT = NW * kWave;
-  const int t0 = tid;
-  const int t1 = tid + NT;
-  const bool m0 = t0 < T && token_slot[t0] == s;
-  const bool m1 = t1 < T && token_slot[t1] == s;
+  const int t0 = lo + tid;
+  const int t1 = lo + tid + NT;
+  const bool m0 = t0 < hi && ids[t0] == s;
+  const bool m1 = t1 < hi && ids[t1] == s;
   const uint64_t b0 = __ballot(m0);
   const uint64_t b1 = __ballot(m1);
   if (lane == 0) {
@@ -330,22 +330,22 @@ __device__ __forceinline__ int nth_set_bit(uint64_t mask, int k) {
 
 // The decode pieces' form of slot_tokens, per wave and with no workgroup
 // barrier (each wave starts its loads as soon as it has its tokens, as with
-// token_order): the wave reads the T slot ids (T <= 1024, one 64-token group
-// per load), takes one ballot per group, and lane row m picks the m-th match
-// (0 when the slot has m tokens or fewer: such rows are not live). n receives
-// the slot's token count (uniform).
-__device__ __forceinline__ int wave_slot_token(const int32_t* __restrict__ token_slot, int T,
+// token_order): the wave reads ids[lo, hi) (at most 1024, one 64-token group
+// per load), takes one ballot per group, and lane row m picks the m-th t with
+// ids[t] == s (0 when there are m or fewer: such rows are not live). n
+// receives the count (uniform).
+__device__ __forceinline__ int wave_slot_token(const int32_t* __restrict__ ids, int lo, int hi,
                                                int s, int m, int& n) {
   constexpr int kMaxGroups = 16;
   const int lane = lane_id();
-  const int ng = (T + kWave - 1) / kWave;
+  const int ng = (hi - lo + kWave - 1) / kWave;
   int v[kMaxGroups];
 #pragma unroll
   for (int g = 0; g < kMaxGroups; ++g) {
     v[g] = -1;
     if (g < ng) {
-      const int t = g * kWave + lane;
-      v[g] = t < T ? token_slot[t] : -1;
+      const int t = lo + g * kWave + lane;
+      v[g] = t < hi ? ids[t] : -1;
     }
   }
   int count = 0;
@@ -355,7 +355,7 @@ __device__ __forceinline__ int wave_slot_token(const int32_t* __restrict__ token
     if (g < ng) {
       const uint64_t mask = __ballot(v[g] == s);
       const int c = __popcll(mask);
-      if (m >= count && m < count + c) tok = g * kWave + nth_set_bit(mask, m - count);
+      if (m >= count && m < count + c) tok = lo + g * kWave + nth_set_bit(mask, m - count);
       count += c;
     }
   }
@@ -785,13 +785,25 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
 
 }  // namespace
 
-// FS (the one-launch form): the slot addressing is built in this launch.
-// Workgroup 0 runs the one-wave sort into order_out / indptr_out for later
-// calls on the same batch (workgroups 1-7 leave at once, so that the pieces
-// keep their XCD placement), and every piece finds its slot's tokens from
-// token_slot itself (slot_tokens); nothing in the launch reads the
-// addressing it writes. Needs T <= 2 * NW * 64 and slots + 1 <= 64.
-template <int RT, int NW, bool FS>
+// MODE kFromSlots / kFromExperts (the one-launch forms): the slot
+// addressing is built in this launch. Workgroup 0 runs a one-wave sort into
+// order_out / indptr_out for later calls on the same batch (workgroups 1-7
+// leave at once, so that the pieces keep their XCD placement), and every
+// piece finds its tokens from the ids itself; nothing in the launch reads
+// the addressing it writes.
+//  * kFromSlots: token_slot holds each token's slot. Needs T <= 2 * NW * 64
+//    and slots + 1 <= 64.
+//  * kFromExperts: token_slot holds each row's slot within its expert
+//    (row_slot) and expert_offs the E + 1 bounds of the expert-sorted rows;
+//    pool entry (virtual slot) e * eslots + s, of `slots` = E * eslots. A
+//    piece of entry (e, s) scans rows [offs[e], offs[e + 1]) for row_slot ==
+//    s: for non-decreasing bounds exactly the rows the keys (expert_key) give
+//    the entry. Needs T <= 2 * NW * 64, E + 1 <= 64 and slots + 1 <= 1024.
+constexpr int kFromAddr = 0;
+constexpr int kFromSlots = 1;
+constexpr int kFromExperts = 2;
+
+template <int RT, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     const void* __restrict__ x_, void* __restrict__ y_, int T, int in, SliceTable st,
     const void* __restrict__ a_, const void* __restrict__ b_, int slots, int R,
@@ -800,7 +812,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     int n_shrink, int n_expand, int nclass, int KP, uint64_t* __restrict__ part,
     uint32_t* __restrict__ tickets, int spin_limit, int early,
     const int32_t* __restrict__ token_slot, int32_t* __restrict__ order_out,
-    int32_t* __restrict__ indptr_out) {
+    int32_t* __restrict__ indptr_out, const int32_t* __restrict__ expert_offs, int E,
+    int eslots) {
   using L = Lds<RT, NW>;
   constexpr int RP = RT * 16;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -817,14 +830,30 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   const int SR = S * R;
   const int out = st.off[S];
   int bid = blockIdx.x;
-  int* tcnt = (int*)red + kWave;   // slot_tokens' counts (red is free until a product)
-  if constexpr (FS) {
+  // LDS while red is free (before any product): kFromSlots: the slot
+  // histogram [64], then slot_tokens' counts; kFromExperts: the key
+  // histogram [1024], the expert bounds [64], then the counts
+  int* tcnt = (int*)red + (MODE == kFromExperts ? 1088 : kWave);
+  int* soffs = (int*)red + 1024;
+  if constexpr (MODE != kFromAddr) {
     if (bid < 8) {
       if (bid == 0 && w == 0) {
-        if (T <= 4 * kWave)
-          addressing_one_wave<4>(token_slot, T, slots, order_out, indptr_out, (int*)red);
-        else
-          addressing_one_wave<2 * NW>(token_slot, T, slots, order_out, indptr_out, (int*)red);
+        if constexpr (MODE == kFromSlots) {
+          if (T <= 4 * kWave)
+            addressing_one_wave<4>(token_slot, T, slots, order_out, indptr_out, (int*)red);
+          else
+            addressing_one_wave<2 * NW>(token_slot, T, slots, order_out, indptr_out, (int*)red);
+        } else {
+          for (int i = lane; i <= E; i += kWave) soffs[i] = expert_offs[i];
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          auto raw_of = [&](int t) { return expert_key(t, token_slot[t], soffs, E, eslots); };
+          if (T <= 4 * kWave)
+            addressing_one_wave_keys<4>(raw_of, T, slots, order_out, indptr_out, (int*)red);
+          else
+            addressing_one_wave_keys<2 * NW>(raw_of, T, slots, order_out, indptr_out,
+                                             (int*)red);
+        }
       }
       return;
     }
@@ -857,10 +886,17 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     // compiler from waiting on the segment bounds before requesting it
     const int r_raw = __builtin_nontemporal_load(ranks + s);
     int seg0 = 0, n, tm = 0;
-    if constexpr (FS)
-      tm = wave_slot_token(token_slot, T, s, lane & 15, n);
-    else
+    if constexpr (MODE == kFromSlots) {
+      tm = wave_slot_token(token_slot, 0, T, s, lane & 15, n);
+    } else if constexpr (MODE == kFromExperts) {
+      const int e = s / eslots;
+      int lo = expert_offs[e], hi = expert_offs[e + 1];
+      lo = min(max(lo, 0), T);
+      hi = min(max(hi, lo), T);
+      tm = wave_slot_token(token_slot, lo, hi, s - e * eslots, lane & 15, n);
+    } else {
       segment_of(indptr, s, T, seg0, n);
+    }
     const int r = clamp_rank(r_raw, R);
     if (r == 0 || n == 0 || n > kMT) return;
     if (nclass > 1 && cls != (2 * r > R ? 0 : 4 * r > R ? 1 : 2)) return;
@@ -876,7 +912,7 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     d.KP = KP;
     d.spin_limit = spin_limit;
     d.early = early;
-    d.tok_given = FS;
+    d.tok_given = MODE != kFromAddr;
     d.tok_m = tm;
     d.lg = RT == 1 ? 0u : RT == 2 ? 1u : RT == 4 ? 2u : RT == 8 ? 3u : 4u;
     const rsrc_t a_r = make_rsrc((const char*)a_ + ((int64_t)s * SR + (int64_t)i * R) * in * 2,
@@ -900,8 +936,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   }
 
   // prefill item: a block of 16 tokens of a long segment, every slice and column
-  int* hist = (int*)red;   // FS: per-slot token counts of the batch
-  if constexpr (FS) {
+  int* hist = (int*)red;   // one-launch forms: per-slot token counts of the batch
+  if constexpr (MODE == kFromSlots) {
     if (tid < kWave) hist[tid] = 0;
     __syncthreads();
     for (int t = tid; t < T; t += NW * kWave) {
@@ -909,10 +945,19 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
       if (v >= 0 && v < slots) atomicAdd(hist + v, 1);
     }
     __syncthreads();
+  } else if constexpr (MODE == kFromExperts) {
+    for (int i = tid; i <= slots; i += NW * kWave) hist[i] = 0;
+    for (int i = tid; i <= E; i += NW * kWave) soffs[i] = expert_offs[i];
+    __syncthreads();
+    for (int t = tid; t < T; t += NW * kWave) {
+      const int v = expert_key(t, token_slot[t], soffs, E, eslots);
+      if (v >= 0) atomicAdd(hist + v, 1);
+    }
+    __syncthreads();
   }
   auto count = [&](int ss) -> int {
     int b0, nn;
-    if constexpr (FS)
+    if constexpr (MODE != kFromAddr)
       nn = hist[ss];
     else
       segment_of(indptr, ss, T, b0, nn);
@@ -924,8 +969,14 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
   const int s = it.slot;
   const int r = clamp_rank(ranks[s], R);
   const int mb = it.local;
-  if constexpr (FS) {
-    slot_tokens<NW>(token_slot, T, s, mb * kMT, -1, tok, tcnt, tid, lane, w);
+  if constexpr (MODE == kFromSlots) {
+    slot_tokens<NW>(token_slot, 0, T, s, mb * kMT, -1, tok, tcnt, tid, lane, w);
+  } else if constexpr (MODE == kFromExperts) {
+    const int e = s / eslots;
+    int lo = soffs[e], hi = soffs[e + 1];
+    lo = min(max(lo, 0), T);
+    hi = min(max(hi, lo), T);
+    slot_tokens<NW>(token_slot, lo, hi, s - e * eslots, mb * kMT, -1, tok, tcnt, tid, lane, w);
   } else {
     int seg0, n;
     segment_of(indptr, s, T, seg0, n);
@@ -1054,23 +1105,19 @@ int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-const void* fused_kernel(int rt, bool fs) {
-  if (fs) {
-    switch (rt) {
-      case 1: return (const void*)k_apply_fused<1, kNW, true>;
-      case 2: return (const void*)k_apply_fused<2, kNW, true>;
-      case 4: return (const void*)k_apply_fused<4, kNW, true>;
-      case 8: return (const void*)k_apply_fused<8, kNW, true>;
-      default: return (const void*)k_apply_fused<16, kNW, true>;
-    }
-  }
+const void* fused_kernel(int rt, int mode) {
+#define K(RTV)                                                                  \
+  (mode == kFromExperts ? (const void*)k_apply_fused<RTV, kNW, kFromExperts>   \
+   : mode == kFromSlots ? (const void*)k_apply_fused<RTV, kNW, kFromSlots>     \
+                        : (const void*)k_apply_fused<RTV, kNW, kFromAddr>)
   switch (rt) {
-    case 1: return (const void*)k_apply_fused<1, kNW, false>;
-    case 2: return (const void*)k_apply_fused<2, kNW, false>;
-    case 4: return (const void*)k_apply_fused<4, kNW, false>;
-    case 8: return (const void*)k_apply_fused<8, kNW, false>;
-    default: return (const void*)k_apply_fused<16, kNW, false>;
+    case 1: return K(1);
+    case 2: return K(2);
+    case 4: return K(4);
+    case 8: return K(8);
+    default: return K(16);
   }
+#undef K
 }
 
 // Workgroups of a kernel instance that the current device holds at once
@@ -1178,6 +1225,13 @@ bool fused_from_slots_supported(int T, int slots) {
   return T <= 2 * kNW * kWave && slots + 1 <= kWave;
 }
 
+bool fused_from_experts_supported(int T, int E, int eslots) {
+  // slot_tokens covers 2 * 512 rows; the bounds (64) and the key histogram
+  // (1024) share the first 1088 words of the reduction area
+  return T <= 2 * kNW * kWave && E >= 1 && eslots >= 1 && E + 1 <= kWave &&
+         (int64_t)E * eslots + 1 <= 1024;
+}
+
 bool fused_supported(int dtype, const SliceTable& st, int R, int T, int in) {
   if (dtype != kDtypeBF16) return false;
   // buffer offsets are 32-bit: every resource must stay below 2 GiB
@@ -1197,14 +1251,20 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
                               hipStream_t stream, const int32_t* token_slot, int32_t* order_out,
-                              int32_t* indptr_out) {
+                              int32_t* indptr_out, const int32_t* expert_offs, int E,
+                              int eslots) {
   if (T == 0) return hipSuccess;
-  const bool fs = token_slot != nullptr;
-  if (fs && !fused_from_slots_supported(T, slots)) return hipErrorInvalidValue;
+  const int mode = token_slot == nullptr ? kFromAddr
+                   : expert_offs != nullptr ? kFromExperts : kFromSlots;
+  const bool fs = mode != kFromAddr;
+  if (mode == kFromSlots && !fused_from_slots_supported(T, slots)) return hipErrorInvalidValue;
+  if (mode == kFromExperts &&
+      (!fused_from_experts_supported(T, E, eslots) || slots != E * eslots))
+    return hipErrorInvalidValue;
   const ChunkTable ct = make_chunks(st, R, slots);
   const int rt = rt_bucket(R);
   const size_t lds = lds_bytes(rt, kNW);
-  const void* fn = fused_kernel(rt, fs);
+  const void* fn = fused_kernel(rt, mode);
   if (lds > 65536) {
     hipError_t e =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1244,30 +1304,30 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   // 38.8 -> 37.4 us (down); on grids that run at once (the 32-slot decode,
   // a router's logits) the reads cost ~0.3 us
   const int early = n_shrink + n_expand > 1024 ? 1 : 0;
-#define LAUNCH(RTV, FSV)                                                                        \
+#define LAUNCH(RTV, MV)                                                                         \
   do {                                                                                          \
-    hipLaunchKernelGGL((k_apply_fused<RTV, kNW, FSV>), dim3((unsigned)grid), dim3(kNW * 64),    \
+    hipLaunchKernelGGL((k_apply_fused<RTV, kNW, MV>), dim3((unsigned)grid), dim3(kNW * 64),     \
                        lds, stream, x, y, T, in, st, a, b, slots, R, token_order, indptr,       \
                        ranks, scalings, ct, (int)n_shrink, (int)n_expand, nclass, KP, part,     \
-                       tickets, spin_limit, early, token_slot, order_out, indptr_out);          \
+                       tickets, spin_limit, early, token_slot, order_out, indptr_out,           \
+                       expert_offs, E, eslots);                                                 \
   } while (0)
-  if (fs) {
-    switch (rt) {
-      case 1: LAUNCH(1, true); break;
-      case 2: LAUNCH(2, true); break;
-      case 4: LAUNCH(4, true); break;
-      case 8: LAUNCH(8, true); break;
-      default: LAUNCH(16, true); break;
-    }
-  } else {
-    switch (rt) {
-      case 1: LAUNCH(1, false); break;
-      case 2: LAUNCH(2, false); break;
-      case 4: LAUNCH(4, false); break;
-      case 8: LAUNCH(8, false); break;
-      default: LAUNCH(16, false); break;
-    }
+#define LAUNCH_RT(MV)                 \
+  switch (rt) {                       \
+    case 1: LAUNCH(1, MV); break;     \
+    case 2: LAUNCH(2, MV); break;     \
+    case 4: LAUNCH(4, MV); break;     \
+    case 8: LAUNCH(8, MV); break;     \
+    default: LAUNCH(16, MV); break;   \
   }
+  if (mode == kFromExperts) {
+    LAUNCH_RT(kFromExperts)
+  } else if (mode == kFromSlots) {
+    LAUNCH_RT(kFromSlots)
+  } else {
+    LAUNCH_RT(kFromAddr)
+  }
+#undef LAUNCH_RT
 #undef LAUNCH
   return hipGetLastError();
 }

@@ -497,4 +497,73 @@ lora_status lora_apply_linear_from_slots(int dtype, const void* x, void* y, int6
                    slot_indptr, ranks, scalings, workspace, s);
 }
 
+int lora_apply_linear_from_experts_one_launch(int dtype, int64_t rows, int64_t in_features,
+                                              const int64_t* out_slices, int32_t num_slices,
+                                              int32_t num_experts, int32_t slots, int32_t R) {
+  if (num_experts < 1 || slots < 1 || (int64_t)num_experts * slots > 8192)
+    return -LORA_ERR_UNSUPPORTED;
+  const int path = lora_apply_linear_path(dtype, rows, in_features, out_slices, num_slices, R);
+  if (path < 0) return path;
+  return path == LORA_PATH_FUSED && rows > 0 &&
+         lora::fused_from_experts_supported((int)rows, num_experts, slots);
+}
+
+size_t lora_apply_linear_from_experts_workspace_bytes(int64_t rows, int64_t in_features,
+                                                      int32_t num_experts, int32_t slots,
+                                                      int32_t num_slices, int32_t R) {
+  if (num_experts < 1 || slots < 1 || (int64_t)num_experts * slots > 8192) return 0;
+  const size_t a =
+      lora_apply_linear_workspace_bytes(rows, in_features, num_experts * slots, num_slices, R);
+  const size_t b = lora_build_addressing_experts_workspace_bytes(rows, num_experts, slots);
+  if (a == 0) return 0;
+  // the apply's region, then the expert addressing's (keys and the sort)
+  return align256(a) + b;
+}
+
+lora_status lora_apply_linear_from_experts(
+    int dtype, const void* x, void* y, int64_t rows, int64_t in_features,
+    const int64_t* out_slices, int32_t num_slices, const void* a, const void* b,
+    int32_t num_experts, int32_t slots, int32_t R, const int32_t* row_slot,
+    const int32_t* expert_offsets, int32_t* token_order, int32_t* slot_indptr,
+    const int32_t* ranks, const float* scalings, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (num_experts < 1 || slots < 1 || (int64_t)num_experts * slots > 8192)
+    return LORA_ERR_UNSUPPORTED;
+  const int32_t K = num_experts * slots;   // pool entries
+  lora_status st = check_common(dtype, rows, K, R);
+  if (st != LORA_OK) return st;
+  SliceTable tab;
+  if ((st = make_slices(dtype, out_slices, num_slices, R, &tab)) != LORA_OK) return st;
+  if (in_features < 1 || in_features > kMaxI32) return LORA_ERR_INVALID_ARG;
+  if (!slot_indptr || !expert_offsets) return LORA_ERR_INVALID_ARG;
+  const size_t need = lora_apply_linear_from_experts_workspace_bytes(rows, in_features,
+                                                                     num_experts, slots,
+                                                                     num_slices, R);
+  if (!workspace || workspace_bytes < need) return LORA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t apply_need =
+      align256(lora_apply_linear_workspace_bytes(rows, in_features, K, num_slices, R));
+  char* ws_addr = static_cast<char*>(workspace) + apply_need;
+  if (rows == 0)   // the addressing of an empty batch: slot_indptr all zeros
+    return hip_status(lora::launch_build_addressing_experts(
+        nullptr, expert_offsets, num_experts, 0, slots, nullptr, slot_indptr, ws_addr,
+        need - apply_need, s));
+  if (!x || !y || !a || !b || !scalings || !row_slot) return LORA_ERR_INVALID_ARG;
+  if ((st = check_addr(token_order, slot_indptr, ranks)) != LORA_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(a) || !aligned16(b)) return LORA_ERR_ALIGNMENT;
+  if (in_features % vec_elems(dtype) != 0) return LORA_ERR_ALIGNMENT;
+  if (lora_apply_linear_from_experts_one_launch(dtype, rows, in_features, out_slices,
+                                                num_slices, num_experts, slots, R) == 1)
+    return hip_status(lora::launch_apply_fused(
+        x, y, (int)rows, (int)in_features, tab, a, b, K, R, nullptr, nullptr, ranks, scalings,
+        workspace, s, row_slot, token_order, slot_indptr, expert_offsets, num_experts, slots));
+  const hipError_t e = lora::launch_build_addressing_experts(
+      row_slot, expert_offsets, num_experts, (int)rows, slots, token_order, slot_indptr,
+      ws_addr, need - apply_need, s);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  return run_apply(dtype, x, y, rows, in_features, tab, num_slices, a, b, K, R, token_order,
+                   slot_indptr, ranks, scalings, workspace, s);
+}
+
 }  // extern "C"

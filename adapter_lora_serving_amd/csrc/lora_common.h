@@ -420,4 +420,80 @@ __device__ __forceinline__ void addressing_one_wave(const int32_t* __restrict__ 
   }
 }
 
+
+// Expert of row r of an expert-sorted batch: the e with offs[e] <= r <
+// offs[e + 1] (binary search over the E + 1 bounds); its key e * slots +
+// row_slot, or -1 (dead) for a slot outside [0, slots) or a row outside
+// [offs[0], offs[E]). Malformed bounds give wrong keys but no access out of
+// bounds.
+__device__ __forceinline__ int expert_key(int r, int s, const int32_t* offs, int E, int slots) {
+  int key = -1;
+  if (r >= offs[0] && r < offs[E]) {
+    int lo = 0, hi = E;   // invariant: offs[lo] <= r < offs[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offs[mid] <= r) lo = mid; else hi = mid;
+    }
+    if (s >= 0 && s < slots) key = lo * slots + s;
+  }
+  return key;
+}
+
+// The one-wave sort over up to 1023 live keys (K), for a batch of at most
+// G * 64 tokens: raw_of(t) gives token t's key (outside [0, K): dead). As
+// addressing_one_wave, with the count histogram of every key in LDS (`hist`:
+// K + 1 ints) and the scan over the K + 1 counts taken in per-lane runs of
+// consecutive keys. Same output as the sort of those keys.
+template <int G, class RawFn>
+__device__ __forceinline__ void addressing_one_wave_keys(RawFn raw_of, int T, int K,
+                                                         int32_t* __restrict__ token_order,
+                                                         int32_t* __restrict__ slot_indptr,
+                                                         int* hist) {
+  const int lane = lane_id();
+  for (int i = lane; i <= K; i += kWave) hist[i] = 0;
+  int raw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    raw[g] = t < T ? raw_of(t) : -1;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int nbits = 32 - __clz(K);
+  int key[G], off[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    const GroupMatch m = match_raw(raw[g], t < T, K, nbits);
+    key[g] = m.key < 0 ? 0 : m.key;   // lanes past T: any valid index, never used
+    off[g] = hist[key[g]] + m.rank;
+    __builtin_amdgcn_wave_barrier();
+    if (m.leader) hist[m.key] += m.count;   // distinct keys: no two leaders collide
+    __builtin_amdgcn_wave_barrier();
+  }
+  // exclusive scan of the K + 1 counts: lane i takes keys [i C, (i + 1) C)
+  const int C = (K + 1 + kWave - 1) / kWave;
+  int sum = 0;
+  for (int j = 0; j < C; ++j) {
+    const int k = lane * C + j;
+    if (k <= K) sum += hist[k];
+  }
+  int run = wave_inclusive_scan(sum) - sum;
+  __builtin_amdgcn_wave_barrier();
+  for (int j = 0; j < C; ++j) {
+    const int k = lane * C + j;
+    if (k <= K) {
+      const int c = hist[k];
+      slot_indptr[k] = run;
+      hist[k] = run;
+      run += c;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = g * kWave + lane;
+    if (t < T) token_order[hist[key[g]] + off[g]] = t;
+  }
+}
+
 }  // namespace lora

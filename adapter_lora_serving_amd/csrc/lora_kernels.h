@@ -112,8 +112,12 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
                               const int32_t* token_order, const int32_t* indptr,
                               const int32_t* ranks, const float* scalings, void* workspace,
                               hipStream_t stream, const int32_t* token_slot = nullptr,
-                              int32_t* order_out = nullptr, int32_t* indptr_out = nullptr);
+                              int32_t* order_out = nullptr, int32_t* indptr_out = nullptr,
+                              const int32_t* expert_offs = nullptr, int E = 0, int eslots = 0);
 bool fused_from_slots_supported(int T, int slots);
+// With expert_offs as well, token_slot holds each row's slot within its
+// expert and `slots` = E * eslots pool entries (the expert addressing).
+bool fused_from_experts_supported(int T, int E, int eslots);
 
 // The base projection y = x @ W^T of a fused linear layer (W [out, in], the
 // shards stacked along out) with the LoRA delta of h (fp32 [T, S*R], from

@@ -6,7 +6,9 @@ addressing build, then the fused shrink + expand (lora_apply_linear) of a
 linear target, or gather_shrink + expand of an embedding target. Where the
 library does both in one launch (lora_apply_linear_from_slots: a bf16 batch
 of at most 1024 tokens over at most 63 slots) the step is that one call,
-which also writes the addressing for the step's later targets. The default
+which also writes the addressing for the step's later targets; an
+expert-sorted batch likewise (lora_apply_linear_from_experts: fewer than 1024
+rows, at most 63 experts and 1023 pool entries). The default
 workload is the decode BGMV batch: T=256 tokens, one per request, in=4096,
 fused q/k/v out_slices (4096, 1024, 1024), 32 adapter slots with ranks in
 {8, 16} (R=16), scaling 2, bf16, seeded synthetic data. `--config 3|4|5`
@@ -411,11 +413,23 @@ def main():
     # in its own launch (lora_apply_linear_from_slots): the step is then one
     # kernel, which also writes token_order and slot_indptr for the step's
     # later targets. Elsewhere the addressing kernel runs first.
-    one_launch = (not tg.embedding and ex is None and L.from_slots_one_launch(
-        1 if wl.dtype == "bf16" else 0, wl.T, tg.in_features, tg.out_slices, wl.slots, wl.R))
+    # (lora_apply_linear_from_experts likewise for an expert-sorted batch)
+    code = 1 if wl.dtype == "bf16" else 0
+    if tg.embedding:
+        one_launch = False
+    elif ex is None:
+        one_launch = L.from_slots_one_launch(code, wl.T, tg.in_features, tg.out_slices,
+                                             wl.slots, wl.R)
+    else:
+        one_launch = L.from_experts_one_launch(code, wl.T, tg.in_features, tg.out_slices,
+                                               ex["experts"], ex["slots"], wl.R)
     if one_launch:
-        need_fs = int(L.lib().lora_apply_linear_from_slots_workspace_bytes(
-            wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R))
+        if ex is None:
+            need_fs = int(L.lib().lora_apply_linear_from_slots_workspace_bytes(
+                wl.T, tg.in_features, wl.slots, tg.num_slices, wl.R))
+        else:
+            need_fs = int(L.lib().lora_apply_linear_from_experts_workspace_bytes(
+                wl.T, tg.in_features, ex["experts"], ex["slots"], tg.num_slices, wl.R))
         ws_fs = torch.zeros(max(need_fs, 256), dtype=torch.uint8, device=dev)
 
     def step_two_launch(i):
@@ -427,8 +441,13 @@ def main():
         if not one_launch:
             return step_two_launch(i)
         s = sets[i % n_sets]
-        L.apply_linear_from_slots_(s["x"], s["y"], s["a"], s["b"], s["ts"], ranks, scal,
-                                   tg.out_slices, out=s["addr"], workspace=ws_fs)
+        if ex is None:
+            L.apply_linear_from_slots_(s["x"], s["y"], s["a"], s["b"], s["ts"], ranks, scal,
+                                       tg.out_slices, out=s["addr"], workspace=ws_fs)
+        else:
+            L.apply_linear_from_experts_(s["x"], s["y"], s["a"], s["b"], s["rs"], s["offs"],
+                                         ex["experts"], ex["slots"], ranks, scal,
+                                         tg.out_slices, out=s["addr"], workspace=ws_fs)
 
     def addr_only(i):
         s = sets[i % n_sets]
@@ -472,11 +491,14 @@ def main():
     ms_apply = timed(g_apply) / K
     ms_addr = timed(g_addr) / K
     ms_two = timed(g_two) / K if one_launch else None
-    # the dominant kernel: the step's one launch (it also reads token_slot,
-    # counted in the metadata term, and writes the addressing), else the apply
+    # the dominant kernel: the step's one launch (it also reads the slot ids,
+    # counted in the metadata term, and the expert bounds, and writes the
+    # addressing), else the apply
     if one_launch:
         ms_kernel = ms_step
         kernel_bytes = alg_bytes + 4 * wl.T + 4 * (wl.slots + 1)
+        if ex is not None:
+            kernel_bytes += 4 * (ex["experts"] + 1)
     else:
         ms_kernel = ms_apply
         kernel_bytes = alg_bytes
@@ -535,7 +557,9 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": ("lora_gather_shrink + lora_expand" if tg.embedding else
-                       "lora_apply_linear_from_slots" if one_launch else "lora_apply_linear"),
+                       "lora_apply_linear" if not one_launch else
+                       "lora_apply_linear_from_slots" if ex is None else
+                       "lora_apply_linear_from_experts"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -305,6 +305,54 @@ int lora_apply_linear_from_slots_one_launch(int dtype, int64_t T, int64_t in_fea
                                             int32_t slots, int32_t R);
 
 /*
+ * lora_apply_linear_from_experts: lora_build_addressing_experts followed by
+ * lora_apply_linear over the num_experts * slots pool entries, for the first
+ * expert target of a step.
+ *
+ * Source: spark_model/lora/expert_apply.rs, experts injection shape (the
+ * expert delta of each routed row, per expert and adapter slot) with the
+ * addressing and apply of lora.backend, LoraBackend.apply_linear_. rows
+ * tokens (rows of the expert-sorted batch) with row_slot (device, int32
+ * [rows]: each row's adapter slot; outside [0, slots): no adapter) and
+ * expert_offsets (device, int32 [num_experts + 1]: expert e owns rows
+ * [offsets[e], offsets[e + 1])); a, b, ranks and scalings are laid out per
+ * pool entry e * slots + slot, as for lora_apply_linear with num_experts *
+ * slots slots. token_order (device, int32 [rows]) and slot_indptr (device,
+ * int32 [num_experts * slots + 1]) receive exactly what
+ * lora_build_addressing_experts writes, and y, for non-decreasing
+ * expert_offsets, exactly what lora_apply_linear gives with that addressing
+ * (other offsets keep every access in bounds but leave y unspecified).
+ * Where lora_apply_linear_from_experts_one_launch(...) is 1 (the fused path
+ * of a small bf16 batch: rows <= 1024, num_experts <= 63, num_experts *
+ * slots <= 1023) it is one kernel launch; elsewhere the addressing kernels
+ * run first, then lora_apply_linear's. workspace: at least
+ * lora_apply_linear_from_experts_workspace_bytes(...) bytes under
+ * lora_apply_linear's rules. rows == 0 writes slot_indptr (all zeros) only.
+ */
+lora_status lora_apply_linear_from_experts(
+    int dtype, const void* x, void* y, int64_t rows, int64_t in_features,
+    const int64_t* out_slices, int32_t num_slices, const void* a, const void* b,
+    int32_t num_experts, int32_t slots, int32_t R, const int32_t* row_slot,
+    const int32_t* expert_offsets, int32_t* token_order, int32_t* slot_indptr,
+    const int32_t* ranks, const float* scalings, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes lora_apply_linear_from_experts needs (0 on bad input). */
+size_t lora_apply_linear_from_experts_workspace_bytes(int64_t rows, int64_t in_features,
+                                                      int32_t num_experts, int32_t slots,
+                                                      int32_t num_slices, int32_t R);
+
+/*
+ * lora_apply_linear_from_experts_one_launch: 1 when
+ * lora_apply_linear_from_experts runs as one kernel launch for these sizes,
+ * 0 when the addressing kernels run first, a negated lora_status for bad
+ * arguments (host-only query).
+ */
+int lora_apply_linear_from_experts_one_launch(int dtype, int64_t rows, int64_t in_features,
+                                              const int64_t* out_slices, int32_t num_slices,
+                                              int32_t num_experts, int32_t slots, int32_t R);
+
+/*
  * lora_column_linear: the base projection of a fused column-parallel linear
  * layer, y = x @ W^T, on the library's bf16 MFMA GEMM.
  *

@@ -272,6 +272,58 @@ def test_from_slots_validation_and_path(lib):
     assert call(ws=A16 + 16) == ALIGN
 
 
+def test_from_experts_validation_and_path(lib):
+    """The routed-expert one-launch form refuses bad host arguments before any
+    launch, sizes its workspace as the apply's (over experts x slots pool
+    entries) plus the expert addressing's, and is one launch exactly for the
+    fused path of fewer than 1024 rows, at most 63 experts and 1023 pool
+    entries."""
+    gu = _slices(14336, 14336)
+    one = lib.lora_apply_linear_from_experts_one_launch
+    assert one(1, 512, 4096, gu, 2, 8, 32, 16) == 1
+    assert one(1, 1023, 256, _slices(64), 1, 63, 16, 16) == 1
+    assert one(1, 600, 256, _slices(64), 1, 1, 1023, 16) == 1
+    assert one(1, 600, 256, _slices(64), 1, 64, 8, 16) == 0       # 65 bounds
+    assert one(1, 600, 256, _slices(64), 1, 32, 32, 16) == 0      # 1024 pool entries
+    assert one(1, 1024, 256, _slices(64), 1, 8, 16, 16) == 0      # segment tiles
+    assert one(0, 512, 256, _slices(64), 1, 8, 16, 16) == 0       # fp32
+    assert one(1, 0, 256, _slices(64), 1, 8, 16, 16) == 0
+    assert one(1, 512, 256, _slices(64), 1, 0, 16, 16) == -UNSUPPORTED
+    assert one(1, 512, 256, _slices(64), 1, 128, 128, 16) == -UNSUPPORTED   # > 8192 entries
+
+    wsb = lib.lora_apply_linear_from_experts_workspace_bytes
+    apply_need = lib.lora_apply_linear_workspace_bytes(512, 4096, 256, 2, 16)
+    addr_need = lib.lora_build_addressing_experts_workspace_bytes(512, 8, 32)
+    assert addr_need > 0
+    assert wsb(512, 4096, 8, 32, 2, 16) == (apply_need + 255) // 256 * 256 + addr_need
+    assert wsb(512, 4096, 0, 32, 2, 16) == 0
+    assert wsb(-1, 4096, 8, 32, 2, 16) == 0
+    need = wsb(512, 4096, 8, 32, 2, 16)
+
+    f = lib.lora_apply_linear_from_experts
+
+    def call(dtype=1, x=A16, T=512, inf=4096, E=8, S=32, R=16, rs=A16, offs=A16, order=A16,
+             indptr=A16, ranks=A16, ws=A16, nbytes=need):
+        return f(dtype, x, A16, T, inf, gu, 2, A16, A16, E, S, R, rs, offs, order, indptr, ranks,
+                 A16, ws, nbytes, None)
+
+    assert call(dtype=5) == UNSUPPORTED
+    assert call(E=0) == UNSUPPORTED
+    assert call(S=9000) == UNSUPPORTED
+    assert call(R=0) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(indptr=None) == INVALID
+    assert call(offs=None) == INVALID
+    assert call(rs=None) == INVALID
+    assert call(order=None) == INVALID
+    assert call(ranks=None) == INVALID
+    assert call(x=None) == INVALID
+    assert call(x=MIS) == ALIGN
+    assert call(ws=None) == WORKSPACE
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(ws=A16 + 16) == ALIGN
+
+
 def test_noalloc_limits_checked_on_host(lib):
     """lora_apply_linear_noalloc refuses sizes beyond its static scratch array
     (LORA_ERR_SCRATCH_LIMIT) and bad scalars (as lora_apply_linear does)
