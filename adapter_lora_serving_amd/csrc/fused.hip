@@ -48,6 +48,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -1289,7 +1290,12 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
   const int nclass = rt_bucket(R) >= 4 ? 3 : 1;
   const int64_t n_shrink = nclass * slots8 * st.n * KP;
   const int64_t n_expand = nclass * slots8 * ct.n;
-  const int64_t n_prefill = (T + kMT - 1) / kMT + slots;
+  // prefill items: only slots with more than kMT tokens have any, at most
+  // T / (kMT + 1) of them, each ceil(n / kMT) < n / kMT + 1 items, so at
+  // most ceil(T / kMT) + min(slots, T / (kMT + 1)) in all (items past the
+  // total leave at once)
+  const int64_t n_prefill =
+      (T + kMT - 1) / kMT + std::min<int64_t>(slots, (int64_t)T / (kMT + 1));
   const int64_t grid = n_shrink + n_expand + n_prefill + (fs ? 8 : 0);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   uint32_t* tickets = (uint32_t*)workspace;
