@@ -124,6 +124,34 @@ def test_random_one_launch(seed):
     _check(wl, wl.target(target), f"random {seed}", expect_one=True)
 
 
+def _ranked(seed, R):
+    """A seeded expert-sorted batch at rank R: the routing of a small MoE
+    (with dead rows, bad slots and an empty expert), and adapters drawn at
+    rank R with per-entry ranks in [0, R] (0 and R included)."""
+    base = _routing(seed, T=160, experts=4, slots=8, hidden=64, inter=64, topk=2)
+    e = base.experts
+    K = e["experts"] * e["slots"]
+    rng = np.random.default_rng(9000 + seed)
+    ranks = rng.integers(0, R + 1, size=K)
+    ranks[0], ranks[1] = 0, R
+    keys = O.expert_keys(e["row_slot"], e["offsets"], e["experts"], e["slots"])
+    wl = W.make_workload(name="experts_ranked", dtype="bf16", T=base.T, in_features=264,
+                         out_slices=(128, 48), R=R, slots=K, ranks=ranks,
+                         scalings=rng.uniform(0.5, 2.0, size=K), token_slot=keys, seed=seed,
+                         rng=rng, target_name="expert_gate_up")
+    wl.experts = e
+    return wl
+
+
+@pytest.mark.parametrize("R", [8, 32, 64, 128, 256])
+def test_rank_buckets_one_launch(R):
+    """Every rank bucket of the fused kernel's expert mode (1, 2, 4, 8 and 16
+    rank tiles)."""
+    log(f"from_experts rank {R}")
+    wl = _ranked(40 + R, R)
+    _check(wl, wl.targets[0], f"rank {R}", expect_one=True)
+
+
 LIMITS = {
     # 63 experts, 1008 pool entries; 1022 rows; 1 row
     "E63": dict(T=300, experts=63, slots=16, hidden=128, inter=256, topk=2),
