@@ -36,6 +36,8 @@
 #include "lora_kernels.h"
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 namespace lora {
@@ -626,9 +628,52 @@ int sgmv_kparts(int in) {
   // ~1024-deep parts, but at least 4 (each >= 256 deep) for a shallow `in`,
   // where one part per token block leaves too few items to fill the GPU:
   // measured on a TP=8 down share (in 1792, 8192 tokens): 1 part 66 us,
-  // 4 parts 55 us, 8 parts 58 us
+  // 4 parts 55 us, 8 parts 58 us. The workspace is sized for this count;
+  // sgmv_kparts_for may launch fewer.
   const int kp = std::max(in / 1024, std::min(4, in / 256));
   return kp < 1 ? 1 : kp > 16 ? 16 : kp;
+}
+
+namespace {
+
+// Compute units of the current device (cached per device); 0 if the runtime
+// cannot say.
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  cache[dev] = cus;
+  return cus;
+}
+
+}  // namespace
+
+int sgmv_kparts_for(int T, int in, int slots, int S) {
+  // A batch of long segments (two or more 128-token blocks per slot on
+  // average) whose items per K part (token blocks x slices, a bound on the
+  // blocks x slice groups) number at most half the compute units: as many K
+  // parts as keep every item on a compute unit of its own (at most
+  // sgmv_kparts(in)). A few more items than compute units leaves a second,
+  // short round on a few of them. Measured at 8192 tokens over 16 slots
+  // (<= 80 blocks, so 3 parts for one slice on 256 compute units), apply per
+  // launch: down (in 14336) 95.6-96.3 us against 101.0-101.6 us with 14
+  // parts (4 parts 111 us, 6 parts 97.4 us); in 1792 (the TP=8 down share)
+  // 52.3-52.5 against 54.7-54.9 us with 4; in 4096 to 12288 3 parts best
+  // too. Two slices at 3 parts (480 items): TP=8 gate/up 1 us slower than
+  // with 4, so a two-slice target keeps sgmv_kparts(in).
+  const int kmax = sgmv_kparts(in);
+  if ((int64_t)T < (int64_t)2 * kBMs * slots) return kmax;
+  const int cus = device_cus();
+  const int64_t per_part = (((int64_t)T + kBMs - 1) / kBMs + slots) * std::max(1, S);
+  if (cus <= 0 || 2 * per_part > cus) return kmax;
+  return (int)std::min<int64_t>(kmax, cus / per_part);
 }
 
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
