@@ -193,7 +193,7 @@ lora_status shrink_impl(int dtype, const void* x, int64_t T, int64_t in_features
     const size_t need = lora_shrink_workspace_bytes(T, in_features, num_slices, R);
     if (workspace_bytes < need) return LORA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LORA_ERR_ALIGNMENT;
-    if (need > 0) kparts = lora::sgmv_kparts_for((int)T, (int)in_features, slots, num_slices);
+    if (need > 0) kparts = lora::sgmv_kparts_for((int)T, (int)in_features, slots, num_slices, R);
   }
   // per-segment choice on the device. bf16: in a small batch, segments of at
   // most kLongSegment tokens on the decode tiles and longer ones on the SGMV
@@ -244,7 +244,7 @@ lora_status run_apply(int dtype, const void* x, void* y, int64_t T, int64_t in_f
       e = lora::launch_apply_fused(x, y, (int)T, (int)in_features, tab, a, b, slots, R,
                                    token_order, slot_indptr, ranks, scalings, workspace, s);
     } else {
-      const int kp = lora::sgmv_kparts_for((int)T, (int)in_features, slots, num_slices);
+      const int kp = lora::sgmv_kparts_for((int)T, (int)in_features, slots, num_slices, R);
       float* parts = h + ws_h_bytes(T, num_slices, R) / sizeof(float);
       e = lora::launch_sgmv_shrink(x, (int)T, (int)in_features, a, slots, num_slices, R,
                                    token_order, slot_indptr, ranks, h, parts, kp, 0, s);

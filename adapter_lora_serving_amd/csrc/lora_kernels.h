@@ -69,9 +69,11 @@ bool sgmv_supported(int dtype, const SliceTable& st, int R, int T, int in);
 // kparts > 1 splits K: the parts go to `parts` (kparts * T * S * R floats)
 // and are summed into h in part order.
 int sgmv_kparts(int in);
-// K parts to launch for a batch of T tokens over `slots` and S slices (at
-// most sgmv_kparts(in), which sizes the workspace).
-int sgmv_kparts_for(int T, int in, int slots, int S);
+// K parts to launch for a batch of T tokens over `slots`, S slices of
+// rank R (at most sgmv_kparts(in), which sizes the workspace).
+int sgmv_kparts_for(int T, int in, int slots, int S, int R);
+// Rank tiles of the shrink kernel launched for such a batch.
+int sgmv_shrink_rt(int T, int slots, int S, int R);
 hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int slots, int S,
                               int R, const int32_t* order, const int32_t* indptr,
                               const int32_t* ranks, float* h, float* parts, int kparts,

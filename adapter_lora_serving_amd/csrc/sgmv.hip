@@ -655,23 +655,43 @@ int device_cus() {
 
 }  // namespace
 
-int sgmv_kparts_for(int T, int in, int slots, int S) {
-  // A batch of long segments (two or more 128-token blocks per slot on
-  // average) whose items per K part (token blocks x slices, a bound on the
-  // blocks x slice groups) number at most half the compute units: as many K
-  // parts as keep every item on a compute unit of its own (at most
-  // sgmv_kparts(in)). A few more items than compute units leaves a second,
-  // short round on a few of them. Measured at 8192 tokens over 16 slots
-  // (<= 80 blocks, so 3 parts for one slice on 256 compute units), apply per
-  // launch: down (in 14336) 95.6-96.3 us against 101.0-101.6 us with 14
-  // parts (4 parts 111 us, 6 parts 97.4 us); in 1792 (the TP=8 down share)
-  // 52.3-52.5 against 54.7-54.9 us with 4; in 4096 to 12288 3 parts best
-  // too. Two slices at 3 parts (480 items): TP=8 gate/up 1 us slower than
-  // with 4, so a two-slice target keeps sgmv_kparts(in).
+int sgmv_shrink_rt(int T, int slots, int S, int R) {
+  // The rank tiles of R, or, for a batch of long segments (two or more
+  // 128-token blocks per slot on average) whose slices fit one item together
+  // (S x ceil(R / 16) <= 8 tiles), enough tiles for all of them: an item then
+  // reads its x block once for every slice, and the items per K part are
+  // the token blocks. Measured with 3 K parts (240 items) on the TP=8
+  // gate/up share (two slices of rank 64): 70.7-71.5 us against 73.4-74.9
+  // us with one item per slice (4 parts); prefill gate/up 217-223 against
+  // 223 us.
+  const int rt = rt_of(R);
+  if ((int64_t)T < (int64_t)2 * kBMs * slots || S <= 1) return rt;
+  const int tiles = S * ((R + 15) / 16);
+  if (tiles > 8) return rt;
+  int p = 1;
+  while (p < tiles) p *= 2;
+  return std::max(rt, p);
+}
+
+int sgmv_kparts_for(int T, int in, int slots, int S, int R) {
+  // A batch of long segments whose items per K part (token blocks, bounded
+  // by ceil(T / 128) + slots, times the slice groups of an item) number at
+  // most half the compute units: as many K parts as keep every item on a
+  // compute unit of its own (at most sgmv_kparts(in)). A few more items than
+  // compute units leaves a second, short round on a few of them. Measured
+  // at 8192 tokens over 16 slots (<= 80 blocks, so 3 parts on 256 compute
+  // units), apply per launch: down (in 14336) 95.6-96.3 us against
+  // 101.0-101.6 us with 14 parts (4 parts 111 us, 6 parts 97.4 us); in 1792
+  // (the TP=8 down share) 52.3-52.5 against 54.7-54.9 us with 4; in 4096 to
+  // 12288 3 parts best too. With two slices in separate items (480 items at
+  // 3 parts) the TP=8 gate/up share lost 1 us against 4 parts.
   const int kmax = sgmv_kparts(in);
   if ((int64_t)T < (int64_t)2 * kBMs * slots) return kmax;
   const int cus = device_cus();
-  const int64_t per_part = (((int64_t)T + kBMs - 1) / kBMs + slots) * std::max(1, S);
+  const int rt = sgmv_shrink_rt(T, slots, S, R);
+  const int ntr = (R + 15) / 16;
+  const int groups = rt >= S * ntr ? 1 : S;
+  const int64_t per_part = (((int64_t)T + kBMs - 1) / kBMs + slots) * groups;
   if (cus <= 0 || 2 * per_part > cus) return kmax;
   return (int)std::min<int64_t>(kmax, cus / per_part);
 }
@@ -703,7 +723,7 @@ hipError_t launch_sgmv_shrink(const void* x, int T, int in, const void* a, int s
                        in, a, slots, S, R, order, indptr, ranks, dst, kparts, stride, min_len, \
                        gmax);                                                                  \
   } while (0)
-  switch (rt_of(R)) {
+  switch (sgmv_shrink_rt(T, slots, S, R)) {
     case 1: L(1); break;
     case 2: L(2); break;
     case 4: L(4); break;
