@@ -529,6 +529,13 @@ def main():
     ms_copy = timed(g_copy) / K
     del g_copy, pairs
 
+    # the per-launch floor on this stream: the same graph timing around K
+    # launches of a one-element fill, a kernel with no work of its own
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    g_nop = capture(lambda i: one.fill_(1.0), K)
+    ms_nop = timed(g_nop) / K
+    del g_nop, one
+
     achieved = kernel_bytes / (ms_kernel * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_step * 1e-3)
     eprint(f"step {ms_step * 1e3:.2f} us ({'one launch' if one_launch else 'two launches'}; "
@@ -536,7 +543,7 @@ def main():
            f"alone {ms_apply * 1e3:.2f} us"
            + (f", addressing then apply {ms_two * 1e3:.2f} us" if one_launch else "")
            + f"; device copy {copy_gbs:.0f} GB/s; a copy of the same bytes "
-           f"{ms_copy * 1e3:.2f} us")
+           f"{ms_copy * 1e3:.2f} us; an empty launch {ms_nop * 1e3:.2f} us")
 
     result = {
         "metric": "LoRA-delta tokens/sec + achieved HBM GB/s (decode) / MFMA util (prefill)",
@@ -575,6 +582,7 @@ def main():
         "addressing_then_apply_us": round((ms_two if one_launch else ms_step) * 1e3, 3),
         "device_copy_gbs": round(copy_gbs, 1),
         "device_copy_same_bytes_us": round(ms_copy * 1e3, 3),
+        "empty_launch_us": round(ms_nop * 1e3, 3),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, tg, args.cpu_seconds)
