@@ -542,6 +542,54 @@ def test_tp8_prefill_share(name):
     assert_tol(f64(y), y_ref, f"tp8 prefill share {name}")
 
 
+# Long-segment batches (two or more 128-token blocks per slot on average)
+# whose slices fit one shrink item together and whose items per K part fit
+# the compute units: the shrink runs with the rank tiles of every slice in one
+# item, and fewer K parts than the workspace holds.
+LONG_GROUPS = {
+    # three slices of rank <= 16: 3 tiles, one item per token block, 3 parts
+    "qkv_r16": dict(T=8192, in_f=4096, out_slices=(512, 128, 128), R=16, slots=16,
+                    ranks=[16, 8, 16, 0, 8, 16, 16, 8, 16, 8, 8, 16, 16, 8, 16, 16], dead=0.02,
+                    skew=1.2),
+    # two slices of rank 32 (the tiles of R alone would take one per item),
+    # ranks ragged within a tile
+    "pair_r32": dict(T=4096, in_f=8192, out_slices=(256, 256), R=32, slots=8,
+                     ranks=[32, 17, 1, 0, 32, 8, 25, 16], dead=0.05),
+    # four slices of rank 32: 8 tiles in one item
+    "four_r32": dict(T=4096, in_f=2048, out_slices=(128, 128, 64, 192), R=32, slots=8,
+                     ranks=[32, 32, 9, 31, 0, 16, 24, 2], skew=1.2),
+    # one slice of rank 64 with a partial last K step
+    "one_r64": dict(T=8192, in_f=14328, out_slices=(1024,), R=64, slots=16,
+                    ranks=[64, 64, 33, 64, 0, 64, 48, 64, 64, 1, 64, 64, 17, 64, 64, 64]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(LONG_GROUPS))
+def test_long_segment_slice_groups(case):
+    """Every row of y against the oracle for the fused call; the unfused
+    shrink's h against the oracle where read (zeros elsewhere); y of the two
+    paths bit-identical (they make the same slice-group and K-part choice);
+    rows of dead tokens and rank-0 slots untouched, bit for bit."""
+    log(f"long-segment slice groups {case}")
+    t = torch()
+    wl = _custom(7, **LONG_GROUPS[case])
+    tg = wl.targets[0]
+    g = GpuTarget(wl, tg)
+    addr = g.addressing()
+    _, _, y1 = g.run(fused=True, addr=addr)
+    _, h, y2 = g.run(fused=False, addr=addr)
+    h_ref, y_ref = O.run_target(wl, tg)
+    assert_tol(f64(y1), y_ref, f"{case} fused")
+    assert t.equal(y1, y2), f"{case}: fused and unfused y differ"
+    unread = unread_mask(wl, tg.num_slices)
+    hg = f64(h)
+    assert np.all(hg[unread] == 0.0)
+    np.testing.assert_allclose(hg[~unread], h_ref[~unread], rtol=1e-3, atol=1e-3)
+    r = np.array([min(max(int(wl.ranks[s]), 0), wl.R) if 0 <= s < wl.slots else 0
+                  for s in wl.token_slot])
+    assert np.array_equal(f64(y1)[r == 0], O.decode(tg.y0, wl.dtype)[r == 0])
+
+
 @pytest.mark.parametrize("rows,E,slots", [
     (300, 8, 16), (2000, 8, 32), (5000, 64, 64),
     # one row, one expert, 63 and 1023 virtual slots, 1024 and 1025 rows
