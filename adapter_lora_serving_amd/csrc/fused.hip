@@ -455,17 +455,30 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&acc)[RT]
     for (int ii = 0; ii < 4; ++ii) dst[(4 * kg + ii) * RP + nt * 16 + m] = acc[nt][ii];
 }
 
-// Loads of group g of a chunk's expand tiles: wave w takes tiles
-// w + NW*(g*PT + u), u < PT; B ranks at or past r and tiles past the chunk
-// read as zeros (kOOB), y rows of padding tokens too.
+// Tile of group g that wave w handles as its u-th (u < PT). contig: the PT
+// adjacent tiles (g*NW + w)*PT + u, so that a wave's y accesses of a token
+// row cover whole cache lines; else dealt round robin, w + NW*(g*PT + u).
+// Contiguous runs pay where a piece has several tokens and its chunk is one
+// full group of tiles (the 32-slot qkv decode, ~8 tokens per slot: step
+// 12.31 -> 12.05 us); elsewhere round robin is kept (a narrow slice would
+// leave most waves without a tile; the routed-expert gate/up, chunks of two
+// groups, lost 0.9 us with contiguous runs).
+template <int NW, int PT>
+__device__ __forceinline__ int tile_of(int g, int w, int u, bool contig) {
+  return contig ? (g * NW + w) * PT + u : w + NW * (g * PT + u);
+}
+
+// Loads of group g of a chunk's expand tiles (tile_of); B ranks at or past r
+// and tiles past the chunk read as zeros (kOOB), y rows of padding tokens too.
 template <int RT, int NW, int PT>
 __device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R, int r, int lo,
-                                                  int ntiles, bool live, uint32_t yrow, int g,
+                                                  int ntiles, bool live, uint32_t yrow, bool contig,
+                                                  int g,
                                                   s16x4 (&bv)[PT][RT], u32x2 (&yv)[PT], int m,
                                                   int kg, int w) {
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * (g * PT + u);
+    const int tile = tile_of<NW, PT>(g, w, u, contig);
 #pragma unroll
     for (int ks = 0; ks < RT; ++ks) {
       const int kk = ks * 16 + kg * 4;
@@ -477,7 +490,7 @@ __device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R,
   }
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * (g * PT + u);
+    const int tile = tile_of<NW, PT>(g, w, u, contig);
     yv[u] = bload8(y_r, (live && tile < ntiles) ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
                                                 : kOOB);
   }
@@ -486,12 +499,12 @@ __device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R,
 // Products and y update of group g from its loaded tiles.
 template <int RT, int NW, int PT>
 __device__ __forceinline__ void expand_group(rsrc_t y_r, int r, int lo, int ntiles, bool live,
-                                             uint32_t yrow, int g, const s16x4 (&bv)[PT][RT],
+                                             uint32_t yrow, bool contig, int g, const s16x4 (&bv)[PT][RT],
                                              const u32x2 (&yv)[PT], const s16x4 (&hb)[RT],
                                              const s16x4 (&lb)[RT], int kg, int w) {
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
-    const int tile = w + NW * (g * PT + u);
+    const int tile = tile_of<NW, PT>(g, w, u, contig);
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < RT; ++ks) {
@@ -516,7 +529,7 @@ __device__ __forceinline__ void expand_group(rsrc_t y_r, int r, int lo, int ntil
 // chunk costs one load latency, not one per group.
 template <int RT, int NW, int PT>
 __device__ __forceinline__ void expand_chunk(rsrc_t b_r, rsrc_t y_r, int R, int r, int lo,
-                                             int ntiles, bool live, uint32_t yrow,
+                                             int ntiles, bool live, uint32_t yrow, bool contig,
                                              s16x4 (&bv0)[PT][RT], u32x2 (&yv0)[PT],
                                              const uint16_t* hhi, const uint16_t* hlo, int m,
                                              int kg, int w) {
@@ -531,11 +544,11 @@ __device__ __forceinline__ void expand_chunk(rsrc_t b_r, rsrc_t y_r, int R, int 
   if constexpr (RT <= 2) {
     // small ranks: a decode chunk is one group (NW * PT tiles); a wider one
     // (a tuning override) takes its further groups one after another
-    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, 0, bv0, yv0, hb, lb, kg, w);
+    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, contig, 0, bv0, yv0, hb, lb, kg, w);
     for (int g = 1; g < ngroups; ++g) {
-      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g, bv0, yv0, m, kg,
+      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, contig, g, bv0, yv0, m, kg,
                                     w);
-      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g, bv0, yv0, hb, lb, kg, w);
+      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, contig, g, bv0, yv0, hb, lb, kg, w);
     }
     return;
   }
@@ -543,14 +556,14 @@ __device__ __forceinline__ void expand_chunk(rsrc_t b_r, rsrc_t y_r, int R, int 
   u32x2 yv1[PT];
   for (int g = 0; g < ngroups; g += 2) {
     if (g + 1 < ngroups)
-      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g + 1, bv1, yv1, m,
+      load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, contig, g + 1, bv1, yv1, m,
                                     kg, w);
-    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g, bv0, yv0, hb, lb, kg, w);
+    expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, contig, g, bv0, yv0, hb, lb, kg, w);
     if (g + 1 < ngroups) {
       if (g + 2 < ngroups)
-        load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, g + 2, bv0, yv0, m,
+        load_expand_group<RT, NW, PT>(b_r, y_r, R, r, lo, ntiles, live, yrow, contig, g + 2, bv0, yv0, m,
                                       kg, w);
-      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, g + 1, bv1, yv1, hb, lb, kg, w);
+      expand_group<RT, NW, PT>(y_r, r, lo, ntiles, live, yrow, contig, g + 1, bv1, yv1, hb, lb, kg, w);
     }
   }
 }
@@ -600,8 +613,9 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
 }
 
 // Expand piece (s, chunk [lo, hi) of slice i): `tiles` are the KP partial
-// tiles of (s, i), `cnts` their ticket counters.
-template <int RT, int NW>
+// tiles of (s, i), `cnts` their ticket counters. CONTIG: the tile order of
+// tile_of, a compile-time choice so that each order's addresses fold.
+template <int RT, int NW, bool CONTIG>
 __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rsrc_t b_r, int r,
                                              float scale, int seg0, int n, int lo, int hi,
                                              const uint64_t* tiles, uint32_t* cnts, float* red,
@@ -619,12 +633,13 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   const bool live = m < n;
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
+  const bool contig = CONTIG;
 
   // group 0 of the chunk: B tiles, then the y rows (which need the token id)
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
-  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, 0, bv, yv, m, kg, w);
+  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 0, bv, yv, m, kg, w);
   // With d.early, one read of this thread's first entry of each tile is
   // issued with the prefetch: when the producers are already done (a piece
   // that starts after them, in a grid larger than the chip holds at once)
@@ -695,7 +710,7 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   }
   __syncthreads();
 
-  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, bv, yv, hhi, hlo, m, kg,
+  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, bv, yv, hhi, hlo, m, kg,
                            w);
 }
 
@@ -755,11 +770,12 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
   const bool live = m < n;
   const int ntiles = (hi - lo) >> 4;
   const int R = d.R;
+  const bool contig = n >= 4 && ntiles == NW * PT;
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
 
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
-  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, 0, bv, yv, m, kg, w);
+  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 0, bv, yv, m, kg, w);
   if (w == 0 && kg == 0) tok[m] = live ? t : -1;
   __syncthreads();
   // h rows: scaled, split into bf16 hi + lo (ranks at or past r read as 0)
@@ -780,7 +796,7 @@ __device__ __forceinline__ void expand_rows(const DecodeArgs& d, rsrc_t b_r, con
   }
   __syncthreads();
 
-  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, bv, yv, hhi, hlo, m, kg,
+  expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, bv, yv, hhi, hlo, m, kg,
                            w);
 }
 
@@ -930,8 +946,15 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     } else {
       const rsrc_t b_r =
           make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
-      expand_piece<RT, NW>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem], tiles,
-                           cnts, red, hhi, hlo, scratch, lane, w, tid);
+      // tile order (tile_of): adjacent runs per wave for a piece of several
+      // tokens whose chunk is one full group of tiles
+      constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;
+      if (n >= 4 && ct.c1[rem] - ct.c0[rem] == 16 * NW * PT)
+        expand_piece<RT, NW, true>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
+                                   tiles, cnts, red, hhi, hlo, scratch, lane, w, tid);
+      else
+        expand_piece<RT, NW, false>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
+                                    tiles, cnts, red, hhi, hlo, scratch, lane, w, tid);
     }
     return;
   }
