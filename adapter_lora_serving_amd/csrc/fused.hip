@@ -74,6 +74,11 @@ struct Lds {
   static constexpr int kHhi = kRed + NW * kMT * RP * 4;
   static constexpr int kHlo = kHhi + kMT * RPS * 2;
   static constexpr int kBytes = kHlo + kMT * RPS * 2;
+  // one-tile kernels: per wave, the A rows of its 8 K steps staged by
+  // buffer-to-LDS transfers (8 blocks of 1 KB), after the regions above
+  static constexpr int kStage = (kBytes + 1023) & ~1023;
+  static constexpr int kStageBytes = RT == 1 ? NW * 8 * 1024 : 0;
+  static constexpr int kTotal = kStage + kStageBytes;
 };
 
 // Sum the NW partial tiles in a fixed order, apply the scaling and split into
@@ -419,6 +424,73 @@ __device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t 
   }
 }
 
+// shrink_steps_n for one rank tile with the A rows staged through LDS: per
+// K-step pair a wave fetches rows 0-7 and 8-15 as two 1 KB blocks of 8 rows
+// x 128 bytes (buffer-to-LDS, lane L: row L / 8, 16-byte chunk L % 8 holding
+// the logical chunk (L % 8) ^ row, so that the operand reads spread over the
+// banks), instead of 16 rows x 64 bytes per load into registers; the operand
+// of lane (m, kg) for step u is then read back from LDS. x is read into
+// registers as in shrink_steps_n. Same products, same order. Measured on
+// the 32-slot qkv decode (shrink pieces alone): the row-major transfers
+// took ~1 us off a 9.2 us launch.
+template <int NW, class XRow>
+__device__ __forceinline__ void shrink_steps_staged(rsrc_t x_r, rsrc_t a_r, uint32_t rowA,
+                                                    int in, XRow xrow_of, int s0, int s1,
+                                                    f32x4* acc, int m, int kg, int w,
+                                                    char* stage) {
+  constexpr int U = 8;
+  int st0 = s0 + w * U;
+  if (st0 >= s1) return;
+  char* wst = stage + w * (U * 1024);
+  const int lane = (kg << 4) | m;
+  const int rl = lane >> 3;            // row of the lane's transfers within a block
+  const int lc = (lane & 7) ^ rl;      // logical chunk the lane fetches
+  bf16x8 xa[U];
+  auto issue_a = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = ((u & 1) << 3) | rl;
+      const int stp = st + (u & ~1);            // first step of the pair
+      const int k = stp * 32 + lc * 8;          // element of the lane's chunk
+      const bool kv = stp + (lc >> 2) < s1 && k < in;
+      dma16(a_r, wst + u * 1024, kv ? (uint32_t)row * rowA + (uint32_t)k * 2u : kOOB);
+    }
+  };
+  auto load_x = [&](int st, uint32_t xrow) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (st + u) * 32 + kg * 8;
+      const bool kv = (st + u) < s1 && k < in && xrow != kOOB;
+      xa[u] = __builtin_bit_cast(bf16x8, bload16(x_r, kv ? xrow + (uint32_t)k * 2u : kOOB));
+    }
+  };
+  auto products = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));   // the transfers into LDS have landed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = ((u & 1) << 2) | kg;       // logical chunk of step u in its pair
+      const int blk = (u & ~1) | (m >> 3);
+      const int r7 = m & 7;
+      const bf16x8 av = *(const bf16x8*)(wst + blk * 1024 + r7 * 128 + ((c ^ r7) << 4));
+      acc[0] = mfma_k32(xa[u], av, acc[0]);
+    }
+  };
+  issue_a(st0);
+  const uint32_t xrow = xrow_of();
+  load_x(st0, xrow);
+  products();
+  for (st0 += NW * U; st0 < s1; st0 += NW * U) {
+    // the operand reads of the previous steps are done before their blocks
+    // are refilled
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+    issue_a(st0);
+    load_x(st0, xrow);
+    products();
+  }
+}
+
 // acc[nt] += x_block . A_rows(nt)^T over K steps [s0, s1) for the rank tiles
 // that hold rows below r, rounded up to a power of two (so at most twice the
 // products are formed, and tiles past r add zeros). One loop per tile count:
@@ -428,7 +500,12 @@ __device__ __forceinline__ void shrink_steps_n(rsrc_t x_r, rsrc_t a_r, uint32_t 
 template <int RT, int NW, class XRow>
 __device__ __forceinline__ void shrink_steps(rsrc_t x_r, rsrc_t a_r, uint32_t rowA, int in,
                                              int r, XRow xrow, int s0, int s1,
-                                             f32x4 (&acc)[RT], int m, int kg, int w) {
+                                             f32x4 (&acc)[RT], int m, int kg, int w,
+                                             char* stage = nullptr) {
+  if constexpr (RT == 1) {
+    if (stage) return shrink_steps_staged<NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w,
+                                              stage);
+  }
   const int ntr = (r + 15) >> 4;
   if constexpr (RT >= 16) {
     if (ntr > 8) return shrink_steps_n<16, NW>(x_r, a_r, rowA, in, xrow, s0, s1, acc, m, kg, w);
@@ -575,7 +652,7 @@ template <int RT, int NW>
 __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, int r, int seg0,
                                              int n, uint64_t* tile, uint32_t* cnt, int nc,
                                              int kp, float* red, int* lds_tag, int lane, int w,
-                                             int tid) {
+                                             int tid, char* stage) {
   constexpr int RP = RT * 16;
   uint32_t ticket = 0;
   if (tid == 0)   // the oldest load in flight: its return is not waited for until the store
@@ -594,7 +671,7 @@ __device__ __forceinline__ void shrink_piece(const DecodeArgs& d, rsrc_t a_r, in
   for (int nt = 0; nt < RT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   shrink_steps<RT, NW>(
       d.x_r, a_r, rowA, d.in, r, [&] { return live ? (uint32_t)t * rowA : kOOB; }, s0, s1, acc,
-      m, kg, w);
+      m, kg, w, stage);
   // the ticket is first used here: the empty statement keeps the compiler
   // from consuming it (and so waiting for the atomic's return) before the
   // bulk loads above are issued
@@ -942,7 +1019,8 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     if (is_shrink) {
       const int kp = rem - i * KP;
       shrink_piece<RT, NW>(d, a_r, r, seg0, n, tiles + kp * kMT * RP, cnts + kp,
-                           ct.per_slice[i], kp, red, scratch, lane, w, tid);
+                           ct.per_slice[i], kp, red, scratch, lane, w, tid,
+                           RT == 1 ? lds + L::kStage : nullptr);
     } else {
       const rsrc_t b_r =
           make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
@@ -1124,6 +1202,14 @@ size_t lds_bytes(int rt, int nw) {
   return 256 + (size_t)nw * kMT * RP * 4 + 2 * (size_t)kMT * (RP + 4) * 2;
 }
 
+// k_apply_fused: the regions above, then (one rank tile) the staged A rows
+// of the decode shrink pieces (Lds::kStage, Lds::kStageBytes)
+size_t fused_lds_bytes(int rt) {
+  static_assert(Lds<1, kNW>::kBytes == 256 + kNW * kMT * 16 * 4 + 2 * kMT * 20 * 2,
+                "host and device LDS layouts");
+  return rt == 1 ? (size_t)Lds<1, kNW>::kTotal : lds_bytes(rt, kNW);
+}
+
 int env_int(const char* name, int dflt) {
   const char* e = getenv(name);
   return e ? atoi(e) : dflt;
@@ -1287,7 +1373,7 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
     return hipErrorInvalidValue;
   const ChunkTable ct = make_chunks(st, R, slots);
   const int rt = rt_bucket(R);
-  const size_t lds = lds_bytes(rt, kNW);
+  const size_t lds = fused_lds_bytes(rt);
   const void* fn = fused_kernel(rt, mode);
   if (lds > 65536) {
     hipError_t e =
