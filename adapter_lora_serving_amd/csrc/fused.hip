@@ -552,7 +552,7 @@ __device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R,
                                                   int ntiles, bool live, uint32_t yrow, bool contig,
                                                   int g,
                                                   s16x4 (&bv)[PT][RT], u32x2 (&yv)[PT], int m,
-                                                  int kg, int w) {
+                                                  int kg, int w, bool load_y = true) {
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int tile = tile_of<NW, PT>(g, w, u, contig);
@@ -565,11 +565,70 @@ __device__ __forceinline__ void load_expand_group(rsrc_t b_r, rsrc_t y_r, int R,
       bv[u][ks] = __builtin_bit_cast(s16x4, bload8(b_r, off));
     }
   }
+  if (!load_y) return;
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int tile = tile_of<NW, PT>(g, w, u, contig);
     yv[u] = bload8(y_r, (live && tile < ntiles) ? yrow + (uint32_t)(lo + tile * 16 + 4 * kg) * 2u
                                                 : kOOB);
+  }
+}
+
+// y rows of a wave's run of 8 adjacent tiles (128 columns, 256 bytes per
+// token row) for up to 16 tokens, staged through LDS: 4 buffer-to-LDS
+// transfers of 8 rows x 128 bytes (block 2h + row group: half h of the
+// span, rows 0-7 or 8-15; lane L fetches row L / 8 and the logical chunk
+// (L % 8) ^ row into its 16-byte slot) instead of 8 loads of 16 rows x 32
+// bytes into registers. yrow is the lane's own token row offset (rows m < n
+// live); col0 the run's first column.
+__device__ __forceinline__ void stage_y_run(rsrc_t y_r, uint32_t yrow, int n, int col0,
+                                            char* ys, int lane) {
+  const int rl = lane >> 3;
+  const int lc = (lane & 7) ^ rl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = j >> 1;
+    const int row = ((j & 1) << 3) | rl;
+    const uint32_t yr = (uint32_t)__shfl((int)yrow, row);
+    dma16(y_r, ys + j * 1024,
+          row < n ? yr + (uint32_t)col0 * 2u + (uint32_t)(h * 128 + lc * 16) : kOOB);
+  }
+}
+// Products and y update of a wave's staged run (one rank tile): each tile's
+// new y values go back into the staged blocks in place, then leave in 4
+// stores of 8 rows x 128 bytes (each lane the 16 bytes it fetched), instead
+// of 8 stores of 16 rows x 32 bytes.
+template <int PT>
+__device__ __forceinline__ void expand_run_staged(rsrc_t y_r, uint32_t yrow, int n, int col0,
+                                                  int r, char* ys, const s16x4 (&bv)[PT][1],
+                                                  s16x4 hb, s16x4 lb, int lane) {
+  const int m = lane & 15;
+  const int kg = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+    const s16x4 b4 = mask_b4(bv[u][0], kg * 4, r);
+    o = mfma_k16(b4, hb, o);
+    o = mfma_k16(b4, lb, o);
+    const int blk = ((u >> 2) << 1) | (m >> 3);
+    const int r7 = m & 7;
+    const int ch = ((u & 3) << 1) | (kg >> 1);
+    u32x2* p = (u32x2*)(ys + blk * 1024 + r7 * 128 + ((ch ^ r7) << 4) + (kg & 1) * 8);
+    const u32x2 yy = *p;
+    *p = u32x2{pack_bf16x2(bf16lo(yy.x) + o[0], bf16hi(yy.x) + o[1]),
+               pack_bf16x2(bf16lo(yy.y) + o[2], bf16hi(yy.y) + o[3])};
+  }
+  // a wave's LDS accesses complete in order: the reads below see the writes
+  const int rl = lane >> 3;
+  const int lc = (lane & 7) ^ rl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = j >> 1;
+    const int row = ((j & 1) << 3) | rl;
+    const uint32_t yr = (uint32_t)__shfl((int)yrow, row);
+    const u32x4 v = *(const u32x4*)(ys + j * 1024 + lane * 16);
+    bstore16_out(y_r, row < n ? yr + (uint32_t)col0 * 2u + (uint32_t)(h * 128 + lc * 16) : kOOB,
+                 v);
   }
 }
 
@@ -697,10 +756,13 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
                                              float scale, int seg0, int n, int lo, int hi,
                                              const uint64_t* tiles, uint32_t* cnts, float* red,
                                              uint16_t* hhi, uint16_t* hlo, int* lds_tag, int lane,
-                                             int w, int tid) {
+                                             int w, int tid, char* stage) {
   constexpr int RP = RT * 16;
   constexpr int RPS = RP + 4;
   constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;   // tiles per wave in flight
+  // one rank tile, adjacent runs (one full group of 8 tiles per wave): y
+  // staged through LDS (stage_y_run), 4 KB per wave
+  constexpr bool kStagedY = CONTIG && RT == 1 && PT == 8;
   uint32_t ticket = 0;
   if (tid < d.KP)   // one ticket per partial tile, taken first
     ticket = __hip_atomic_fetch_add(cnts + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -716,7 +778,10 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
-  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 0, bv, yv, m, kg, w);
+  char* ys = stage + w * 4096;
+  load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 0, bv, yv, m, kg,
+                                w, !kStagedY);
+  if constexpr (kStagedY) stage_y_run(d.y_r, yrow, n, lo + w * PT * 16, ys, lane);
   // With d.early, one read of this thread's first entry of each tile is
   // issued with the prefetch: when the producers are already done (a piece
   // that starts after them, in a grid larger than the chip holds at once)
@@ -787,6 +852,13 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   }
   __syncthreads();
 
+  if constexpr (kStagedY) {
+    // the transfers were waited for with the prefetch, before the partials
+    const s16x4 hb = *(const s16x4*)(hhi + m * RPS + kg * 4);
+    const s16x4 lb = *(const s16x4*)(hlo + m * RPS + kg * 4);
+    expand_run_staged<PT>(d.y_r, yrow, n, lo + w * PT * 16, r, ys, bv, hb, lb, lane);
+    return;
+  }
   expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, bv, yv, hhi, hlo, m, kg,
                            w);
 }
@@ -1029,10 +1101,12 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
       constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;
       if (n >= 4 && ct.c1[rem] - ct.c0[rem] == 16 * NW * PT)
         expand_piece<RT, NW, true>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
-                                   tiles, cnts, red, hhi, hlo, scratch, lane, w, tid);
+                                   tiles, cnts, red, hhi, hlo, scratch, lane, w, tid,
+                                   lds + L::kStage);
       else
         expand_piece<RT, NW, false>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
-                                    tiles, cnts, red, hhi, hlo, scratch, lane, w, tid);
+                                    tiles, cnts, red, hhi, hlo, scratch, lane, w, tid,
+                                   lds + L::kStage);
     }
     return;
   }
