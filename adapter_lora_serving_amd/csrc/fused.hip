@@ -533,13 +533,12 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4 (&acc)[RT]
 }
 
 // Tile of group g that wave w handles as its u-th (u < PT). contig: the PT
-// adjacent tiles (g*NW + w)*PT + u, so that a wave's y accesses of a token
-// row cover whole cache lines; else dealt round robin, w + NW*(g*PT + u).
-// Contiguous runs pay where a piece has several tokens and its chunk is one
-// full group of tiles (the 32-slot qkv decode, ~8 tokens per slot: step
-// 12.31 -> 12.05 us); elsewhere round robin is kept (a narrow slice would
-// leave most waves without a tile; the routed-expert gate/up, chunks of two
-// groups, lost 0.9 us with contiguous runs).
+// adjacent tiles (g*NW + w)*PT + u, so that a wave's y of a token row is one
+// contiguous run (staged through LDS, stage_y_run); else dealt round robin,
+// w + NW*(g*PT + u). Adjacent runs are taken for chunks of one or two full
+// groups at one rank tile: alone (y in registers) they took the 32-slot qkv
+// decode step from 12.31 to 12.05 us; with y staged, to 10.8 us. A narrow
+// slice keeps round robin, which leaves no wave without a tile.
 template <int NW, int PT>
 __device__ __forceinline__ int tile_of(int g, int w, int u, bool contig) {
   return contig ? (g * NW + w) * PT + u : w + NW * (g * PT + u);
@@ -763,6 +762,7 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   // one rank tile, adjacent runs (one full group of 8 tiles per wave): y
   // staged through LDS (stage_y_run), 4 KB per wave
   constexpr bool kStagedY = CONTIG && RT == 1 && PT == 8;
+  static_assert(!CONTIG || kStagedY, "adjacent runs are taken only with y staged");
   uint32_t ticket = 0;
   if (tid < d.KP)   // one ticket per partial tile, taken first
     ticket = __hip_atomic_fetch_add(cnts + tid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -778,10 +778,21 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
   s16x4 bv[PT][RT];
   u32x2 yv[PT];
   const uint32_t yrow = (uint32_t)t * (uint32_t)d.out * 2u;
-  char* ys = stage + w * 4096;
+  // staged: one or two full groups (chunks of 1024 or 2048 columns), each
+  // wave's run of group g at stage + 8 KB w + 4 KB g; the B tiles of a second
+  // group are prefetched too
+  char* ys = stage + w * 8192;
+  const int ngs = kStagedY ? ntiles / (NW * PT) : 1;
+  s16x4 bv1[PT][RT];
   load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 0, bv, yv, m, kg,
                                 w, !kStagedY);
-  if constexpr (kStagedY) stage_y_run(d.y_r, yrow, n, lo + w * PT * 16, ys, lane);
+  if constexpr (kStagedY) {
+    if (ngs > 1)
+      load_expand_group<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, 1, bv1, yv,
+                                    m, kg, w, false);
+    for (int gg = 0; gg < ngs; ++gg)
+      stage_y_run(d.y_r, yrow, n, lo + (gg * NW + w) * PT * 16, ys + gg * 4096, lane);
+  }
   // With d.early, one read of this thread's first entry of each tile is
   // issued with the prefetch: when the producers are already done (a piece
   // that starts after them, in a grid larger than the chip holds at once)
@@ -857,6 +868,9 @@ __device__ __forceinline__ void expand_piece(const DecodeArgs& d, rsrc_t a_r, rs
     const s16x4 hb = *(const s16x4*)(hhi + m * RPS + kg * 4);
     const s16x4 lb = *(const s16x4*)(hlo + m * RPS + kg * 4);
     expand_run_staged<PT>(d.y_r, yrow, n, lo + w * PT * 16, r, ys, bv, hb, lb, lane);
+    if (ngs > 1)
+      expand_run_staged<PT>(d.y_r, yrow, n, lo + (NW + w) * PT * 16, r, ys + 4096, bv1, hb, lb,
+                            lane);
     return;
   }
   expand_chunk<RT, NW, PT>(b_r, d.y_r, R, r, lo, ntiles, live, yrow, contig, bv, yv, hhi, hlo, m, kg,
@@ -1096,17 +1110,20 @@ __global__ __launch_bounds__(NW * 64) void k_apply_fused(
     } else {
       const rsrc_t b_r =
           make_rsrc((const char*)b_ + (int64_t)s * out * R * 2, (uint32_t)out * (uint32_t)R * 2u);
-      // tile order (tile_of): adjacent runs per wave for a piece of several
-      // tokens whose chunk is one full group of tiles
-      constexpr int PT = RT <= 2 ? 8 : RT <= 4 ? 4 : RT <= 8 ? 2 : 1;
-      if (n >= 4 && ct.c1[rem] - ct.c0[rem] == 16 * NW * PT)
-        expand_piece<RT, NW, true>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
-                                   tiles, cnts, red, hhi, hlo, scratch, lane, w, tid,
-                                   lds + L::kStage);
-      else
-        expand_piece<RT, NW, false>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
-                                    tiles, cnts, red, hhi, hlo, scratch, lane, w, tid,
-                                   lds + L::kStage);
+      // tile order (tile_of): adjacent runs per wave, y through LDS, for a
+      // chunk of one or two full groups of tiles at one rank tile
+      const int cw = ct.c1[rem] - ct.c0[rem];
+      if constexpr (RT == 1) {
+        if (cw == 16 * NW * 8 || cw == 32 * NW * 8) {
+          expand_piece<RT, NW, true>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem],
+                                     ct.c1[rem], tiles, cnts, red, hhi, hlo, scratch, lane, w,
+                                     tid, lds + L::kStage);
+          return;
+        }
+      }
+      expand_piece<RT, NW, false>(d, a_r, b_r, r, scalings[s], seg0, n, ct.c0[rem], ct.c1[rem],
+                                  tiles, cnts, red, hhi, hlo, scratch, lane, w, tid,
+                                  lds + L::kStage);
     }
     return;
   }
