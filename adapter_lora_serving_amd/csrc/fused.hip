@@ -1472,7 +1472,11 @@ hipError_t launch_apply_fused(const void* x, void* y, int T, int in, const Slice
     if (e != hipSuccess) return e;
   }
   int KP = k_parts(in, st.off[st.n], slots, st.n);
-  if (env_int("LORA_KPARTS", 0) <= 0) {
+  // One rank tile stages A (8 K steps of 32 per wave, 2048 per workgroup):
+  // a part shallower than that leaves waves without steps, so the count
+  // stays at the ~2048-deep rule there (32-slot qkv decode, in 4096: 2 parts
+  // 10.39-10.47 us per step against 10.73 with 3 and 13.2 with 4).
+  if (env_int("LORA_KPARTS", 0) <= 0 && rt != 1) {
     // More K parts while every live piece (one per slot, slice and part, and
     // one per slot and column chunk) still fits on the chip at once, and each
     // part stays at least 1024 deep: more shrink pieces put more loads in
