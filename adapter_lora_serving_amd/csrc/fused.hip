@@ -1345,15 +1345,17 @@ int64_t resident_blocks(const void* fn, int threads, size_t lds) {
 
 int decode_chunk_cols(int R, int out, int slots) {
   // columns per decode expand piece: 1024 up to rank 32, else 2048; twice
-  // that when a batch of many slots would otherwise make more than 4096
+  // that when a batch of many slots would otherwise make more than 512
   // expand pieces, whose fixed cost (ticket, token ids, wait) then dominates
   // (measured on the routed-expert gate/up, 256 pool entries x 28672
-  // outputs: 103.6 -> 93.5 us; the 32-slot qkv decode keeps 1024);
+  // outputs: 103.6 -> 93.5 us; on the routed-expert down, 1024 pieces of
+  // 1024 columns, with y staged: 36.1 -> 34.3-34.7 us; the 32-slot qkv
+  // decode, 192 pieces, keeps 1024: 2048 took 11.8 against 10.7 us);
   // overridable for tuning experiments
   const int env = env_int("LORA_DECODE_CHUNK", 0);
   if (env >= 16 && env % 16 == 0) return env;
   int cols = R <= 32 ? 1024 : 2048;
-  if ((int64_t)slots * ((out + cols - 1) / cols) > 4096) cols *= 2;
+  if ((int64_t)slots * ((out + cols - 1) / cols) > 512) cols *= 2;
   return cols;
 }
 
@@ -1363,13 +1365,15 @@ int k_parts(int in, int out, int slots, int S) {
   // single expand piece, and more, shorter shrink pieces shorten the chain:
   // measured at 64 outputs, 9.5 -> 8.1 us for 2 -> 4 parts; 8 parts 9.4 us);
   // then fewer while the shrink pieces (slots x slices x parts) would number
-  // more than 1024 (the routed-expert down product, 256 pool entries, in
-  // 14336: 7 parts 41.1 us, 4 parts 39.0 us); overridable for tuning
+  // more than 512 (the routed-expert down product, 256 pool entries, in
+  // 14336: 7 parts 41.1 us, 4 parts 39.0 us before A was staged; staged,
+  // 7 / 4 / 3 / 2 parts 39.3 / 36.1 / 36.0 / 35.0 us; its gate/up, 2 slices,
+  // 1 part as fast as 2); overridable for tuning
   const int env = env_int("LORA_KPARTS", 0);
   int kp = env > 0 ? env : in / (out < 1024 ? 1024 : 2048);
   kp = kp < 1 ? 1 : kp > 8 ? 8 : kp;
   if (env <= 0)
-    while (kp > 1 && (int64_t)slots * S * kp > 1024) --kp;
+    while (kp > 1 && (int64_t)slots * S * kp > 512) --kp;
   return kp;
 }
 
